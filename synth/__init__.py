@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for the INT2 KV-cache workloads.
+
+This module is shared by the oracle tests, the GPU parity tests and the
+benchmark.  It only *draws* inputs; it holds none of the method's arithmetic
+(no rotation, clipping, quantization, packing or attention).
+
+Two generators are used:
+
+* Small, host-side tensors (query bases, calibration and decode queries,
+  per-channel key offsets, outlier channels, physical page permutations,
+  ragged context lengths) come from NumPy ``PCG64`` streams, one stream per
+  ``(workload, layer, kv_head, tag)`` tuple.
+
+* Bulk keys and values come from a counter-based generator so that the GPU
+  can draw tens of gigabytes in place and the CPU can redraw any sampled
+  slice bit for bit.  Each 4x32-bit block is Philox4x32-10 as published by
+  Salmon, Moraes, Dror and Shaw ("Parallel random numbers: as easy as 1, 2,
+  3", SC 2011).  A standard-normal-like draw is the Irwin-Hall sum of four
+  16-bit uniforms, centred and scaled by one fp32 multiply; everything after
+  the Philox block is exact integer work plus round-to-nearest-even fp32
+  operations, so a GPU implementation of the same definition
+  (``synth/csrc/gen.hip``) reproduces these values exactly.  Its tails stop at
+  about 3.46 sigma, which is the one way it differs from a true Gaussian.
+
+Key distribution (per KV head): ``k = bf16((z + mu) * m)`` with
+``mu_c ~ N(0, 0.5^2)`` per channel and ``m = 20`` on four distinct seeded
+outlier channels (1 elsewhere).  Values: ``v = bf16(z)``.  Values are meant
+to arrive already rotated by an orthogonal R_V; an orthogonal rotation of an
+isotropic Gaussian vector is again isotropic Gaussian, so drawing ``z``
+directly has the same distribution and keeps the GPU draw bit-exact.
+Queries: ``q = bf16(z * sqrt(lambda) @ B^T)`` with ``lambda_i = 0.9^i`` and a
+Haar-random orthogonal basis ``B`` per KV head.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+
+# Workload ids used to separate seed streams.
+CFG_TINY = 0          # 1 layer, 1 KV head, 2 q heads, 1024 tokens
+CFG_QWEN3_4B = 1      # 32 q / 8 kv heads, batch 8, 32K context
+CFG_QWEN3_8B = 2      # 36 layers, 32 q / 8 kv heads, batch 32, 100K context
+CFG_QWEN3_32B = 3     # 64 q / 8 kv heads, batch 16, ragged 8K..128K
+CFG_PREFILL = 4       # one 131072-token sequence, 8 kv heads
+
+TAG_K, TAG_V = 0, 1
+TAG_QBASIS, TAG_QCAL, TAG_QDEC, TAG_KPARAM = 2, 3, 4, 5
+TAG_PAGES, TAG_LENGTHS, TAG_RV = 6, 7, 8
+
+
+def stream(*ids: int) -> np.random.Generator:
+    """An independent NumPy stream for one ``(cfg, layer, kv_head, tag, ...)`` id."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(i) for i in ids])))
+
+
+def haar(n: int, rng: np.random.Generator) -> np.ndarray:
+    """Haar-random orthogonal n x n matrix (QR of a Gaussian, sign of diag(R) fixed)."""
+    a = rng.standard_normal((n, n))
+    q, r = np.linalg.qr(a)
+    return q * np.sign(np.diag(r))[None, :]
+
+
+# ----------------------------------------------------------------------------- bf16 helpers
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+# ----------------------------------------------------------------------------- host streams
+
+def query_basis(cfg: int, layer: int, kv_head: int) -> np.ndarray:
+    return haar(HEAD_DIM, stream(cfg, layer, kv_head, TAG_QBASIS))
+
+
+def query_spectrum() -> np.ndarray:
+    return 0.9 ** np.arange(HEAD_DIM, dtype=np.float64)
+
+
+def queries(basis: np.ndarray, n: int, rng: np.random.Generator) -> np.ndarray:
+    """n queries with covariance B diag(0.9^i) B^T, rounded to bf16 (uint16 bits)."""
+    z = rng.standard_normal((n, HEAD_DIM))
+    q = (z * np.sqrt(query_spectrum())[None, :]) @ basis.T
+    return f32_to_bf16_bits(q.astype(np.float32))
+
+
+def calibration_queries(cfg: int, layer: int, kv_head: int, n: int = 4096) -> np.ndarray:
+    return queries(query_basis(cfg, layer, kv_head), n, stream(cfg, layer, kv_head, TAG_QCAL))
+
+
+def decode_queries(cfg: int, layer: int, n_seqs: int, n_q_heads: int, n_kv_heads: int,
+                   step: int = 0) -> np.ndarray:
+    """bf16 bits [n_seqs, n_q_heads, 128]; q head h draws from KV head h // (Hq/Hkv)."""
+    g = n_q_heads // n_kv_heads
+    out = np.empty((n_seqs, n_q_heads, HEAD_DIM), dtype=np.uint16)
+    for kv in range(n_kv_heads):
+        basis = query_basis(cfg, layer, kv)
+        rng = stream(cfg, layer, kv, TAG_QDEC, step)
+        out[:, kv * g:(kv + 1) * g, :] = queries(basis, n_seqs * g, rng).reshape(n_seqs, g, HEAD_DIM)
+    return out
+
+
+def key_params(cfg: int, layer: int, kv_head: int):
+    """Per-channel offsets mu (float32 [128]) and multipliers m (float32 [128], 20 on 4 channels)."""
+    rng = stream(cfg, layer, kv_head, TAG_KPARAM)
+    mu = (rng.standard_normal(HEAD_DIM) * 0.5).astype(np.float32)
+    chans = rng.choice(HEAD_DIM, size=4, replace=False)
+    m = np.ones(HEAD_DIM, dtype=np.float32)
+    m[chans] = 20.0
+    return mu, m
+
+
+def page_permutation(cfg: int, layer: int, n_pages: int) -> np.ndarray:
+    return stream(cfg, layer, 0, TAG_PAGES).permutation(n_pages).astype(np.int32)
+
+
+def ragged_lengths(cfg: int, n: int, lo: int, hi: int) -> np.ndarray:
+    return stream(cfg, 0, 0, TAG_LENGTHS).integers(lo, hi + 1, size=n).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------- counter-based bulk draw
+
+_M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
+_W0, _W1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
+_MASK32 = np.uint64(0xFFFFFFFF)
+# sqrt(3) / 65536 rounded to fp32: unit variance for the centred sum of four 16-bit uniforms.
+IH4_SCALE = np.float32(np.sqrt(3.0) / 65536.0)
+IH4_CENTER = 131070  # 4 * 32767.5, rounded down; the draw is centred to within 2^-17 sigma
+
+
+def philox4x32_10(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds on uint32-valued arrays (held in uint64)."""
+    c0, c1, c2, c3 = (np.asarray(c, dtype=np.uint64) & _MASK32 for c in (c0, c1, c2, c3))
+    k0 = np.uint64(int(k0) & 0xFFFFFFFF)
+    k1 = np.uint64(int(k1) & 0xFFFFFFFF)
+    for r in range(10):
+        p0 = _M0 * c0
+        p1 = _M1 * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
+        c0, c1, c2, c3 = (hi1 ^ c1 ^ k0) & _MASK32, lo1, (hi0 ^ c3 ^ k1) & _MASK32, lo0
+        if r < 9:
+            k0 = (k0 + _W0) & _MASK32
+            k1 = (k1 + _W1) & _MASK32
+    return c0, c1, c2, c3
+
+
+def bulk_key(cfg: int, layer: int, kv_head: int, tag: int) -> int:
+    return ((cfg & 0xFF) << 24) | ((layer & 0xFFF) << 12) | ((kv_head & 0xFF) << 4) | (tag & 0xF)
+
+
+def _ih4(wa, wb) -> np.ndarray:
+    s = (wa & np.uint64(0xFFFF)) + (wa >> np.uint64(16)) + (wb & np.uint64(0xFFFF)) + (wb >> np.uint64(16))
+    return (s.astype(np.int64) - IH4_CENTER).astype(np.float32) * IH4_SCALE
+
+
+def bulk_normal(key0: int, key1: int, token0: int, n_tokens: int) -> np.ndarray:
+    """float32 [n_tokens, 128] draws for tokens token0 .. token0+n_tokens-1 of one stream.
+
+    Element (t, c) uses Philox counter (t*64 + c//2, 0, 0, 0); even c takes output
+    words 0,1 and odd c takes words 2,3.
+    """
+    t = np.arange(token0, token0 + n_tokens, dtype=np.uint64)
+    pair = (t[:, None] * np.uint64(64) + np.arange(64, dtype=np.uint64)[None, :]).ravel()
+    zero = np.zeros_like(pair)
+    w0, w1, w2, w3 = philox4x32_10(pair & _MASK32, pair >> np.uint64(32), zero, zero, key0, key1)
+    out = np.empty((pair.size, 2), dtype=np.float32)
+    out[:, 0] = _ih4(w0, w1)
+    out[:, 1] = _ih4(w2, w3)
+    return out.reshape(n_tokens, HEAD_DIM)
+
+
+def bulk_keys(cfg: int, layer: int, seq: int, kv_head: int, token0: int, n_tokens: int,
+              mu: np.ndarray, mult: np.ndarray) -> np.ndarray:
+    """bf16 bits [n_tokens, 128]: k = bf16((z + mu) * m), each step one fp32 RNE op."""
+    z = bulk_normal(bulk_key(cfg, layer, kv_head, TAG_K), seq, token0, n_tokens)
+    x = (z + mu[None, :].astype(np.float32)) * mult[None, :].astype(np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def bulk_values(cfg: int, layer: int, seq: int, kv_head: int, token0: int, n_tokens: int) -> np.ndarray:
+    """bf16 bits [n_tokens, 128]: v = bf16(z)."""
+    z = bulk_normal(bulk_key(cfg, layer, kv_head, TAG_V), seq, token0, n_tokens)
+    return f32_to_bf16_bits(z)
+
+
+def unit_kv(cfg: int, layer: int, seq: int, kv_head: int, n_tokens: int, token0: int = 0):
+    """Keys and values (bf16 bits) of one (layer, seq, kv_head) unit."""
+    mu, m = key_params(cfg, layer, kv_head)
+    return (bulk_keys(cfg, layer, seq, kv_head, token0, n_tokens, mu, m),
+            bulk_values(cfg, layer, seq, kv_head, token0, n_tokens))
