@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the INT2 paged KV cache on one MI355X.
+
+Workload: a Qwen3-8B-shaped model's attention, 36 layers x (32 query heads, 8 KV heads,
+head_dim 128), batch 32, 100000-token context per sequence, INT2 history with a BF16 sink
+(64) and recent window (256), 64-token pages in a shuffled physical order.  Keys and values
+are synthetic (seeded, drawn on the GPU); rotations are calibrated per (layer, KV head) from
+seeded queries.
+
+One step = for every layer: evict the oldest window token of each sequence into INT2, append
+one new token per sequence, run decode attention for all 32 query heads.  Prints one JSON
+line (stdout); progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+METRIC = "INT2 paged decode-attn achieved HBM GB/s (% peak) + steps/s @100K ctx, B=32"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(lens, n2s, hq, hkv):
+    """Algorithmic bytes of one decode_attn call (per layer)."""
+    b = 0
+    for L, n2 in zip(lens, n2s):
+        b += hkv * (80 * n2 + 512 * min(L, 320))
+        b += hq * 128 * (2 + 4)
+        b += 4 * (-(-n2 // 64))
+    return b + hkv * 128 * 128 * 4
+
+
+def evict_bytes(n_seqs, hkv):
+    return n_seqs * (hkv * (512 + 80) + 4)
+
+
+def append_bytes(n_seqs, hkv):
+    return n_seqs * hkv * (512 + 512) + hkv * 128 * 128 * 4
+
+
+def cpu_baseline(rots, lens0, q_layer0, out_layer0, hq, hkv, cfg, context, n_units, total_units, step_bytes_attn):
+    """Time the oracle's decode attention on sampled (layer 0, seq, kv head) units, one core."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    import synth
+    from oracle import attention, store as ostore
+    g = hq // hkv
+    units = [(s, kv) for s, kv in [(0, 0), (17, 5), (31, 3), (9, 7)]][:n_units]
+    t_build = t_dec = 0.0
+    errs = []
+    for s, kv in units:
+        t0 = time.perf_counter()
+        kb, vb = synth.unit_kv(cfg, 0, s, kv, context)
+        st = ostore.OracleStore(1, 1, -(-context // 64), -(-context // 64), range(-(-context // 64)), rots[0][kv:kv + 1])
+        st.write([0], kb[None, :, None, :], vb[None, :, None, :])
+        t1 = time.perf_counter()
+        out = attention.decode_store(st, q_layer0[s:s + 1, kv * g:(kv + 1) * g], [0], 1 / math.sqrt(128), g)
+        t2 = time.perf_counter()
+        t_build += t1 - t0
+        t_dec += t2 - t1
+        ref = out[0]
+        gpu = out_layer0[s, kv * g:(kv + 1) * g]
+        errs.append(float(np.linalg.norm(gpu - ref) / np.linalg.norm(ref)))
+        log(f"cpu oracle unit seq={s} kv={kv}: build {t1 - t0:.1f}s decode {t2 - t1:.2f}s rel-l2 vs gpu {errs[-1]:.2e}")
+    if limiter is not None:
+        limiter.unregister()
+    per_unit = t_dec / len(units)
+    cpu_step_s = per_unit * total_units
+    return {
+        "value": step_bytes_attn / cpu_step_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(units)} of {total_units} (layer, seq, kv-head) units of the attention pass, "
+                   f"{context}-token context each, decode attention only (state building "
+                   f"{t_build / len(units):.1f}s/unit untimed), extrapolated x{total_units}"),
+        "seconds_per_unit": per_unit,
+        "sample_rel_l2_vs_gpu": max(errs),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=36, help="development only: fewer layers")
+    ap.add_argument("--context", type=int, default=100000, help="development only")
+    ap.add_argument("--batch", type=int, default=32, help="development only")
+    ap.add_argument("--attn-reps", type=int, default=3)
+    ap.add_argument("--cpu-units", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the decode step shards by sequence or KV head with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_write_amd as oscar
+    import synth
+    from synth import gpu as sgpu
+
+    oscar.load()
+    torch.cuda.set_device(0)
+    cfg = synth.CFG_QWEN3_8B
+    n_layers, B, ctx = args.layers, args.batch, args.context
+    hq, hkv = 32, 8
+    n_steps_total = args.warmup + args.steps
+    max_pages = -(-(ctx + n_steps_total + 64) // 64)
+    num_pages = B * max_pages
+    full = (n_layers, B, ctx) == (36, 32, 100000)
+
+    # ---- calibration (host, fp64), one R_K per (layer, kv head)
+    t0 = time.time()
+
+    def calib(lh):
+        l, h = lh
+        q = synth.bf16_bits_to_f32(synth.calibration_queries(cfg, l, h))
+        return oscar.oscar_calibrate_host(q)[0]
+
+    with ThreadPoolExecutor(16) as ex:
+        flat = list(ex.map(calib, [(l, h) for l in range(n_layers) for h in range(hkv)]))
+    rots = [np.stack(flat[l * hkv:(l + 1) * hkv]) for l in range(n_layers)]
+    log(f"calibrated {n_layers * hkv} rotations in {time.time() - t0:.1f}s")
+
+    # ---- stores and prefill
+    t0 = time.time()
+    stores = []
+    kbuf = torch.empty((1, ctx, hkv, 128), dtype=torch.int16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    for l in range(n_layers):
+        st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, l, num_pages))
+        st.set_rotation(rots[l])
+        prm = sgpu.HeadParams(cfg, l, hkv)
+        for s in range(B):
+            sgpu.draw_kv(prm, s, 0, ctx, kbuf[0], vbuf[0])
+            st.write([s], kbuf, vbuf)
+        stores.append(st)
+        if l % 6 == 5 or l == n_layers - 1:
+            torch.cuda.synchronize()
+            log(f"prefilled layer {l + 1}/{n_layers} ({time.time() - t0:.1f}s)")
+    del kbuf, vbuf
+    # per-step new tokens, drawn on the GPU up front: [layer][step] -> [B, 1, hkv, 128]
+    newk = torch.empty((n_layers, n_steps_total, B, 1, hkv, 128), dtype=torch.int16, device="cuda")
+    newv = torch.empty_like(newk)
+    tmpk = torch.empty((n_steps_total, hkv, 128), dtype=torch.int16, device="cuda")
+    tmpv = torch.empty_like(tmpk)
+    for l in range(n_layers):
+        prm = sgpu.HeadParams(cfg, l, hkv)
+        for s in range(B):
+            sgpu.draw_kv(prm, s, ctx, n_steps_total, tmpk, tmpv)
+            newk[l, :, s, 0] = tmpk
+            newv[l, :, s, 0] = tmpv
+    qs = [torch.from_numpy(synth.decode_queries(cfg, l, B, hq, hkv).view(np.int16)).cuda() for l in range(n_layers)]
+    seqs = list(range(B))
+    outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ws_bytes = max(st.workspace_bytes(seqs) for st in stores) + (1 << 20)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+
+    # layer-0 decode on the prefill state, kept for the CPU-oracle sample check
+    stores[0].decode(seqs, qs[0], scale, out=outs[0], ws=ws)
+    torch.cuda.synchronize()
+    out_layer0 = outs[0].cpu().numpy()
+    q_layer0 = qs[0].cpu().numpy().view(np.uint16)
+    lens0 = [stores[0].seq_info(s) for s in seqs]
+
+    def step(i):
+        for l in range(n_layers):
+            st = stores[l]
+            st.evict(seqs, 1)
+            st.write(seqs, newk[l, i], newv[l, i])
+            st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+
+    def step_bytes():
+        tot = 0
+        for st in stores:
+            info = [st.seq_info(s) for s in seqs]
+            # state after evict + append of this step: n_int2 + 1, len + 1
+            tot += decode_bytes([L + 1 for L, _ in info], [n2 + 1 for _, n2 in info], hq, hkv)
+            tot += evict_bytes(B, hkv) + append_bytes(B, hkv)
+        return tot
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    bytes_per_step = []
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        bytes_per_step.append(step_bytes())
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    step_gbps = sum(bytes_per_step) / (gpu_ms / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms/step), {step_gbps:.0f} GB/s")
+
+    # ---- attention-only pass over the frozen cache: per-call HIP events on the launch stream
+    per_call = []
+    attn_bytes = []
+    for st in stores:
+        info = [st.seq_info(s) for s in seqs]
+        attn_bytes.append(decode_bytes([L for L, _ in info], [n2 for _, n2 in info], hq, hkv))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
+    for r in range(args.attn_reps):
+        for l, st in enumerate(stores):
+            evs[l][0].record()
+            st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+            evs[l][1].record()
+        torch.cuda.synchronize()
+        per_call.extend(a.elapsed_time(b) for a, b in evs)
+    attn_ms = float(np.mean(per_call))
+    attn_gbps = float(np.mean(attn_bytes)) / (attn_ms / 1e3) / 1e9
+    log(f"attention-only: {attn_ms * 1e3:.1f} us/layer, {attn_gbps:.0f} GB/s ({100 * attn_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "steps_per_s": round(1e3 / ms_per_step, 3),
+        "pct_peak": round(100 * step_gbps / PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; keys/values drawn on the GPU, Philox4x32-10)",
+        "config": {
+            "workload": (f"qwen3-8b-shaped decode step: {n_layers} layers x (evict 1 + append 1 + GQA decode "
+                         f"attention), {hq} q / {hkv} kv heads, head_dim 128, batch {B}, {ctx}-token context, "
+                         "INT2 KV in 64-token pages (shuffled), BF16 sink 64 + window 256"),
+            "layers": n_layers, "batch": B, "context": ctx, "q_heads": hq, "kv_heads": hkv,
+            "headline_config": full,
+        },
+        "attn_only": {"us_per_layer": round(attn_ms * 1e3, 2), "gbps": round(attn_gbps, 1),
+                      "pct_peak": round(100 * attn_gbps / PEAK_GBPS, 2),
+                      "bytes_per_layer": int(np.mean(attn_bytes))},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "decode attention call (split-K kernel + combine), per layer",
+        },
+    }
+    if not args.no_cpu_baseline:
+        total_units = n_layers * B * hkv
+        step_attn_bytes = float(np.sum(attn_bytes))
+        result["cpu_baseline"] = cpu_baseline(rots, lens0, q_layer0, out_layer0, hq, hkv, cfg, ctx,
+                                              args.cpu_units, total_units, step_attn_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,261 @@
+"""Python binding of liboscar (INT2 paged KV cache: write path and fused decode attention, gfx950).
+
+Argument marshalling only: every step of the write and read paths runs in the
+HIP kernels of ``liboscar.so``.  PyTorch provides device memory and the current
+stream.  The functions named like the C ABI (``oscar_calibrate_host``,
+``oscar_kv_write``, ``oscar_kv_evict_window``, ``oscar_decode_attn``) take the
+same arguments as their C counterparts, with tensors in place of pointers;
+``KVStore`` bundles one layer's device buffers and handle.
+
+Loading fails loudly when the library has not been built; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboscar.so")
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+SINK_TOKENS = 64
+WINDOW_TOKENS = 256
+RING_SLOTS = 320
+HEAD_BLOCK = 5120
+FLAG_PLAN_ONLY = 1
+
+OK, E_ARG, E_NOPAGE, E_WINDOW_FULL, E_WINDOW_SHORT, E_NUMERIC, E_HIP, E_WORKSPACE, E_STATE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+_NAMES = {E_ARG: "E_ARG", E_NOPAGE: "E_NOPAGE", E_WINDOW_FULL: "E_WINDOW_FULL", E_WINDOW_SHORT: "E_WINDOW_SHORT",
+          E_NUMERIC: "E_NUMERIC", E_HIP: "E_HIP", E_WORKSPACE: "E_WORKSPACE", E_STATE: "E_STATE"}
+
+EXPORTS = [
+    "oscar_calibrate_host", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
+    "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
+    "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
+    "oscar_kv_set_decode_split", "oscar_last_error", "oscar_kv_destroy",
+]
+
+
+class OscarError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("pool", ctypes.c_void_p), ("ring", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("rot", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load liboscar.so (built in-tree); raises when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: run `python -m decode_attention_write_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "oscar_calibrate_host": [P, I64, I32, P, P],
+        "oscar_kv_buffer_bytes": [P, P, P, P, P],
+        "oscar_kv_create": [P, P, I32, P, P],
+        "oscar_kv_set_rotation": [P, P, P],
+        "oscar_kv_write": [P, P, I32, I32, P, P, P],
+        "oscar_kv_evict_window": [P, P, I32, I32, P],
+        "oscar_decode_workspace_bytes": [P, P, I32, P],
+        "oscar_decode_attn": [P, P, I32, P, ctypes.c_float, P, P, SZ, P],
+        "oscar_kv_seq_info": [P, I32, P, P],
+        "oscar_kv_get_page_table": [P, P],
+        "oscar_kv_free_pages": [P, P, P],
+        "oscar_kv_reset_seq": [P, I32, P],
+        "oscar_kv_set_decode_split": [P, I32],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.oscar_last_error.argtypes = []
+    lib.oscar_last_error.restype = ctypes.c_char_p
+    lib.oscar_kv_destroy.argtypes = [P]
+    lib.oscar_kv_destroy.restype = None
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise OscarError(rc, load().oscar_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _i32(seq_ids):
+    a = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------- C-ABI-named functions
+
+def oscar_calibrate_host(q_rows):
+    """R_K (float32 [128,128]) and descending eigenvalues (float64 [128]) from query rows (host)."""
+    q = np.ascontiguousarray(np.asarray(q_rows, dtype=np.float32))
+    rot = np.empty((HEAD_DIM, HEAD_DIM), dtype=np.float32)
+    eig = np.empty(HEAD_DIM, dtype=np.float64)
+    _check(load().oscar_calibrate_host(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], q.shape[1],
+                                       rot.ctypes.data_as(ctypes.c_void_p), eig.ctypes.data_as(ctypes.c_void_p)))
+    return rot, eig
+
+
+def oscar_kv_write(store, seq_ids, k, v, stream=None):
+    """k, v: bf16 device tensors [n_seqs, n_new, Hkv, 128] (contiguous)."""
+    ids, p = _i32(seq_ids)
+    n_new = int(k.shape[1]) if k is not None else 0
+    _check(load().oscar_kv_write(store.handle, p, len(ids), n_new, _ptr(k), _ptr(v),
+                                 None if store.plan_only else _stream(stream)))
+
+
+def oscar_kv_evict_window(store, seq_ids, n_evict, stream=None):
+    ids, p = _i32(seq_ids)
+    _check(load().oscar_kv_evict_window(store.handle, p, len(ids), int(n_evict),
+                                        None if store.plan_only else _stream(stream)))
+
+
+def oscar_decode_workspace_bytes(store, seq_ids):
+    ids, p = _i32(seq_ids)
+    n = ctypes.c_size_t(0)
+    _check(load().oscar_decode_workspace_bytes(store.handle, p, len(ids), ctypes.byref(n)))
+    return n.value
+
+
+def oscar_decode_attn(store, seq_ids, q, sm_scale, out, ws, stream=None):
+    """q: bf16 [n_seqs, Hq, 128]; out: fp32 [n_seqs, Hq, 128]; ws: device workspace tensor."""
+    ids, p = _i32(seq_ids)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().oscar_decode_attn(store.handle, p, len(ids), _ptr(q), ctypes.c_float(sm_scale), _ptr(out),
+                                    _ptr(ws), nbytes, None if store.plan_only else _stream(stream)))
+
+
+# ---------------------------------------------------------------------------- store object
+
+class KVStore:
+    """One attention layer's store: caller-owned torch device buffers + the liboscar handle."""
+
+    def __init__(self, num_q_heads, num_kv_heads, max_seqs, max_pages_per_seq, num_pages,
+                 free_pages=None, device="cuda", plan_only=False, stream=None):
+        lib = load()
+        self.hq, self.hkv = num_q_heads, num_kv_heads
+        self.max_seqs, self.max_pages, self.num_pages = max_seqs, max_pages_per_seq, num_pages
+        self.plan_only = plan_only
+        d = _Desc(num_q_heads, num_kv_heads, max_seqs, max_pages_per_seq, num_pages,
+                  FLAG_PLAN_ONLY if plan_only else 0, None, None, None, None)
+        sizes = [ctypes.c_size_t(0) for _ in range(4)]
+        _check(lib.oscar_kv_buffer_bytes(ctypes.byref(d), *[ctypes.byref(s) for s in sizes]))
+        self.bytes = {k: s.value for k, s in zip(("pool", "ring", "page_table", "rot"), sizes)}
+        self.pool = self.ring = self.page_table_dev = self.rot = None
+        if not plan_only:
+            import torch
+            self.pool = torch.empty(self.bytes["pool"], dtype=torch.uint8, device=device)
+            self.ring = torch.empty(self.bytes["ring"] // 2, dtype=torch.int16, device=device)
+            self.page_table_dev = torch.empty(self.bytes["page_table"] // 4, dtype=torch.int32, device=device)
+            self.rot = torch.empty(self.bytes["rot"], dtype=torch.uint8, device=device)
+            d.pool, d.ring = self.pool.data_ptr(), self.ring.data_ptr()
+            d.page_table, d.rot = self.page_table_dev.data_ptr(), self.rot.data_ptr()
+        fp = np.arange(num_pages, dtype=np.int32) if free_pages is None else np.asarray(free_pages, dtype=np.int32)
+        fp = np.ascontiguousarray(fp)
+        h = ctypes.c_void_p(0)
+        _check(lib.oscar_kv_create(ctypes.byref(d), fp.ctypes.data_as(ctypes.c_void_p), len(fp),
+                                   None if plan_only else _stream(stream), ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().oscar_kv_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- API
+    def set_rotation(self, rot, stream=None):
+        r = np.ascontiguousarray(np.asarray(rot, dtype=np.float32).reshape(self.hkv, HEAD_DIM, HEAD_DIM))
+        _check(load().oscar_kv_set_rotation(self.handle, r.ctypes.data_as(ctypes.c_void_p),
+                                            None if self.plan_only else _stream(stream)))
+
+    def write(self, seq_ids, k, v, stream=None, n_new=None):
+        if self.plan_only:
+            ids, p = _i32(seq_ids)
+            _check(load().oscar_kv_write(self.handle, p, len(ids), int(n_new), None, None, None))
+            return
+        oscar_kv_write(self, seq_ids, k, v, stream)
+
+    def evict(self, seq_ids, n_evict=1, stream=None):
+        oscar_kv_evict_window(self, seq_ids, n_evict, stream)
+
+    def workspace_bytes(self, seq_ids):
+        return oscar_decode_workspace_bytes(self, seq_ids)
+
+    def decode(self, seq_ids, q, sm_scale, out=None, ws=None, stream=None):
+        import torch
+        n = len(seq_ids)
+        if out is None:
+            out = torch.empty((n, self.hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        if ws is None:
+            ws = torch.empty(max(4, self.workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)
+        oscar_decode_attn(self, seq_ids, q, sm_scale, out, ws, stream)
+        return out
+
+    def seq_info(self, seq):
+        ln, n2 = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(load().oscar_kv_seq_info(self.handle, int(seq), ctypes.byref(ln), ctypes.byref(n2)))
+        return ln.value, n2.value
+
+    def page_table(self):
+        out = np.empty((self.max_seqs, self.max_pages), dtype=np.int32)
+        _check(load().oscar_kv_get_page_table(self.handle, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def free_pages(self):
+        n = ctypes.c_int32(0)
+        _check(load().oscar_kv_free_pages(self.handle, ctypes.byref(n), None))
+        out = np.empty(n.value, dtype=np.int32)
+        _check(load().oscar_kv_free_pages(self.handle, None, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def reset_seq(self, seq, stream=None):
+        _check(load().oscar_kv_reset_seq(self.handle, int(seq), None if self.plan_only else _stream(stream)))
+
+    def set_decode_split(self, pages_per_split):
+        _check(load().oscar_kv_set_decode_split(self.handle, int(pages_per_split)))
+
+    # ---- views of the device buffers (for tests and export)
+    def pool_view(self):
+        return self.pool.view(self.num_pages, self.hkv, HEAD_BLOCK)
+
+    def ring_view(self):
+        return self.ring.view(self.max_seqs, self.hkv, 2, RING_SLOTS, HEAD_DIM)
+
+    def table_view(self):
+        return self.page_table_dev.view(self.max_seqs, self.max_pages)

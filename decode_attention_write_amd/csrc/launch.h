@@ -1,0 +1,82 @@
+// Internal launch interface between the host runtime (oscar_host.cpp) and the
+// HIP kernels.  Per-call plans travel in kernel arguments (at most CHUNK
+// sequences per launch), so a decode step needs no host-to-device copies.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int CHUNK = 64;          // sequences per launch
+constexpr int SCATTER_MAX = 224;   // page-table updates per scatter launch
+
+struct ScatterArgs {
+  int32_t* dst;
+  int32_t n;
+  int32_t idx[SCATTER_MAX];
+  int32_t val[SCATTER_MAX];
+};
+
+struct WriteSeq {
+  int32_t seq;   // sequence slot
+  int32_t len0;  // length before the call
+  int32_t src;   // row of this sequence in the call's k/v arrays
+  int32_t pad;
+};
+
+struct WriteArgs {
+  const uint16_t* k;  // bf16 [n_seqs_call][n_new][hkv][128]
+  const uint16_t* v;
+  uint8_t* pool;
+  uint16_t* ring;
+  const int32_t* page_table;
+  const uint8_t* rot;
+  int32_t hkv, max_pages, n_new, n_seqs;
+  WriteSeq seqs[CHUNK];
+};
+
+struct EvictSeq {
+  int32_t seq;
+  int32_t n_int2;  // INT2 count before the call
+};
+
+struct EvictArgs {
+  uint8_t* pool;
+  uint16_t* ring;
+  const int32_t* page_table;
+  int32_t hkv, max_pages, n_evict, n_seqs;
+  EvictSeq seqs[CHUNK];
+};
+
+struct DecodeSeq {
+  int32_t seq;     // sequence slot
+  int32_t len;     // tokens stored
+  int32_t n_int2;  // INT2 tokens
+  int32_t src;     // row of this sequence in the call's q / out arrays
+};
+
+struct DecodeArgs {
+  const uint16_t* q;      // bf16 [n_seqs_call][hq][128]
+  const uint8_t* pool;
+  const uint16_t* ring;
+  const int32_t* page_table;
+  const uint8_t* rot;
+  float* part;            // [n_seqs][hq][n_split_max][130]: m, l, o[128]
+  float* out;             // fp32 [n_seqs_call][hq][128]
+  int32_t hkv, hq, max_pages, n_seqs;
+  int32_t pages_per_split, n_split_max;
+  float scale_log2;       // sm_scale * log2(e)
+  int32_t pad;
+  DecodeSeq seqs[CHUNK];
+};
+
+constexpr int PART_STRIDE = 130;
+
+hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
+hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s);
+hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace oscar

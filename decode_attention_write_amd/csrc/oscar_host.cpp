@@ -1,0 +1,465 @@
+// Host runtime of liboscar: the store handle, argument validation, the FIFO
+// page allocator with its page-table mirror, split planning and the C ABI.
+//
+// Every call validates completely before it changes anything, so a failing
+// call leaves the store as it was.  All per-call plans travel to the kernels in
+// kernel arguments; the only host-to-device traffic besides that is the
+// rotation upload and page-table updates (small scatter launches).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+#include "oscar.h"
+#include "launch.h"
+
+namespace oscar {
+
+thread_local std::string g_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+}  // namespace oscar
+
+using namespace oscar;
+
+struct oscar_kv {
+  oscar_kv_desc desc;
+  bool plan_only;
+  std::vector<int64_t> len;
+  std::vector<int64_t> n_int2;
+  std::vector<int32_t> table;  // host mirror [max_seqs][max_pages]
+  std::deque<int32_t> fifo;
+  int32_t pages_per_split = 0;
+  bool has_rotation = false;
+};
+
+namespace {
+
+constexpr int64_t kSink = OSCAR_SINK_TOKENS, kWin = OSCAR_WINDOW_TOKENS, kRing = OSCAR_RING_SLOTS;
+constexpr int64_t kPage = OSCAR_PAGE_TOKENS;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return OSCAR_E_HIP;
+}
+
+int check_desc(const oscar_kv_desc* d) {
+  if (!d) { set_error("null descriptor"); return OSCAR_E_ARG; }
+  if (d->num_kv_heads < 1 || d->num_q_heads < d->num_kv_heads || d->num_q_heads % d->num_kv_heads) {
+    set_error("num_q_heads must be a positive multiple of num_kv_heads");
+    return OSCAR_E_ARG;
+  }
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) { set_error("Hq/Hkv must be 1, 2, 4 or 8"); return OSCAR_E_ARG; }
+  if (d->max_seqs < 1 || d->max_pages_per_seq < 1 || d->num_pages < 1) {
+    set_error("max_seqs, max_pages_per_seq and num_pages must be >= 1");
+    return OSCAR_E_ARG;
+  }
+  if (d->flags & ~OSCAR_FLAG_PLAN_ONLY) { set_error("unknown flag bits"); return OSCAR_E_ARG; }
+  return OSCAR_OK;
+}
+
+// seq ids in range and distinct
+int check_seqs(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
+  if (!seq_ids || n_seqs < 1 || n_seqs > kv->desc.max_seqs) {
+    set_error("seq_ids must hold 1..max_seqs entries");
+    return OSCAR_E_ARG;
+  }
+  std::vector<char> seen(kv->desc.max_seqs, 0);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (s < 0 || s >= kv->desc.max_seqs) { set_error("seq id %d out of range", s); return OSCAR_E_ARG; }
+    if (seen[s]) { set_error("seq id %d listed twice", s); return OSCAR_E_ARG; }
+    seen[s] = 1;
+  }
+  return OSCAR_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Push page-table updates to the device in scatter launches.
+int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd, hipStream_t st) {
+  if (kv->plan_only || upd.empty()) return OSCAR_OK;
+  for (size_t i = 0; i < upd.size(); i += SCATTER_MAX) {
+    ScatterArgs a{};
+    a.dst = kv->desc.page_table;
+    a.n = static_cast<int32_t>(std::min<size_t>(SCATTER_MAX, upd.size() - i));
+    for (int k = 0; k < a.n; ++k) {
+      a.idx[k] = upd[i + k].first;
+      a.val[k] = upd[i + k].second;
+    }
+    hipError_t e = launch_scatter(a, st);
+    if (e != hipSuccess) return hip_fail(e, "page-table update");
+  }
+  return OSCAR_OK;
+}
+
+int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
+  if (kv->pages_per_split > 0) return kv->pages_per_split;
+  int64_t total = 0, max_pages = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int64_t p = ceil_div(kv->n_int2[seq_ids[i]], kPage);
+    total += p;
+    max_pages = std::max(max_pages, p);
+  }
+  // aim at ~4 work-groups per compute unit over the whole call (256 CUs)
+  const int64_t target_wg = 1024;
+  const int64_t units = total * kv->desc.num_kv_heads;
+  int64_t pps = std::max<int64_t>(8, ceil_div(units, target_wg));
+  pps = std::min<int64_t>(pps, std::max<int64_t>(1, max_pages));
+  return std::max<int64_t>(1, pps);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_last_error(void) { return g_error.c_str(); }
+
+int oscar_kv_buffer_bytes(const oscar_kv_desc* d, size_t* pool, size_t* ring, size_t* table, size_t* rot) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (pool) *pool = static_cast<size_t>(d->num_pages) * d->num_kv_heads * OSCAR_HEAD_BLOCK;
+  if (ring) *ring = static_cast<size_t>(d->max_seqs) * d->num_kv_heads * 2 * kRing * OSCAR_HEAD_DIM * 2;
+  if (table) *table = static_cast<size_t>(d->max_seqs) * d->max_pages_per_seq * 4;
+  if (rot) *rot = static_cast<size_t>(d->num_kv_heads) * OSCAR_ROT_HEAD_BYTES;
+  return OSCAR_OK;
+}
+
+int oscar_kv_create(const oscar_kv_desc* d, const int32_t* free_pages, int32_t n_free, void* stream, oscar_kv** out) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!out || (n_free > 0 && !free_pages) || n_free < 0 || n_free > d->num_pages) {
+    set_error("oscar_kv_create: bad free list or output pointer");
+    return OSCAR_E_ARG;
+  }
+  const bool plan = (d->flags & OSCAR_FLAG_PLAN_ONLY) != 0;
+  if (!plan && (!d->pool || !d->ring || !d->page_table || !d->rot)) {
+    set_error("oscar_kv_create: device buffers must be set (or OSCAR_FLAG_PLAN_ONLY)");
+    return OSCAR_E_ARG;
+  }
+  std::vector<char> seen(d->num_pages, 0);
+  for (int i = 0; i < n_free; ++i) {
+    const int p = free_pages[i];
+    if (p < 0 || p >= d->num_pages || seen[p]) {
+      set_error("oscar_kv_create: free page %d out of range or repeated", p);
+      return OSCAR_E_ARG;
+    }
+    seen[p] = 1;
+  }
+  oscar_kv* kv = new oscar_kv();
+  kv->desc = *d;
+  kv->plan_only = plan;
+  kv->len.assign(d->max_seqs, 0);
+  kv->n_int2.assign(d->max_seqs, 0);
+  kv->table.assign(static_cast<size_t>(d->max_seqs) * d->max_pages_per_seq, -1);
+  kv->fifo.assign(free_pages, free_pages + n_free);
+  if (!plan) {
+    hipError_t e = launch_fill_i32(d->page_table, static_cast<int64_t>(kv->table.size()), -1, as_stream(stream));
+    if (e != hipSuccess) {
+      delete kv;
+      return hip_fail(e, "oscar_kv_create: page-table fill");
+    }
+  }
+  *out = kv;
+  return OSCAR_OK;
+}
+
+void oscar_kv_destroy(oscar_kv* kv) { delete kv; }
+
+int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
+  if (!kv || !rot_host) { set_error("oscar_kv_set_rotation: null argument"); return OSCAR_E_ARG; }
+  const int hkv = kv->desc.num_kv_heads;
+  const size_t n = static_cast<size_t>(hkv) * OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(rot_host[i])) { set_error("oscar_kv_set_rotation: non-finite entry"); return OSCAR_E_NUMERIC; }
+  if (kv->plan_only) { kv->has_rotation = true; return OSCAR_OK; }
+  // per head: fp32 R, then three bf16 terms r0 + r1 + r2 ~= R (each the bf16 rounding of the remainder)
+  std::vector<uint8_t> blob(static_cast<size_t>(hkv) * OSCAR_ROT_HEAD_BYTES);
+  const size_t dd = OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
+  auto to_bf16 = [](float x) -> uint16_t {
+    uint32_t u;
+    std::memcpy(&u, &x, 4);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  };
+  auto from_bf16 = [](uint16_t b) -> float {
+    uint32_t u = static_cast<uint32_t>(b) << 16;
+    float x;
+    std::memcpy(&x, &u, 4);
+    return x;
+  };
+  for (int h = 0; h < hkv; ++h) {
+    uint8_t* base = blob.data() + static_cast<size_t>(h) * OSCAR_ROT_HEAD_BYTES;
+    std::memcpy(base, rot_host + h * dd, dd * 4);
+    uint16_t* terms = reinterpret_cast<uint16_t*>(base + dd * 4);
+    for (size_t i = 0; i < dd; ++i) {
+      float rem = rot_host[h * dd + i];
+      for (int t = 0; t < 3; ++t) {
+        const uint16_t b = to_bf16(rem);
+        terms[t * dd + i] = b;
+        rem = rem - from_bf16(b);
+      }
+    }
+  }
+  hipError_t e = hipMemcpyAsync(kv->desc.rot, blob.data(), blob.size(), hipMemcpyHostToDevice, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "oscar_kv_set_rotation: upload");
+  // the host blob dies at return: make sure the (pageable) copy has consumed it
+  e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "oscar_kv_set_rotation: sync");
+  kv->has_rotation = true;
+  return OSCAR_OK;
+}
+
+int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t n_new, const void* k,
+                   const void* v, void* stream) {
+  if (!kv) { set_error("oscar_kv_write: null handle"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (n_new < 1) { set_error("oscar_kv_write: n_new must be >= 1"); return OSCAR_E_ARG; }
+  if (!kv->plan_only && (!k || !v)) { set_error("oscar_kv_write: null k or v"); return OSCAR_E_ARG; }
+  if (!kv->has_rotation) { set_error("oscar_kv_write: rotation not set"); return OSCAR_E_STATE; }
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  int64_t need = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (kv->len[s] == 0) {
+      const int64_t pages = ceil_div(std::max<int64_t>(0, n_new - kRing), kPage);
+      if (pages > maxp) {
+        set_error("oscar_kv_write: sequence %d would need %lld pages > max_pages_per_seq", s, static_cast<long long>(pages));
+        return OSCAR_E_NOPAGE;
+      }
+      need += pages;
+    } else {
+      const int64_t new_len = kv->len[s] + n_new;
+      const int64_t win = std::max<int64_t>(0, new_len - kSink - kv->n_int2[s]);
+      if (win > kWin) {
+        set_error("oscar_kv_write: window of sequence %d would hold %lld > 256 tokens", s, static_cast<long long>(win));
+        return OSCAR_E_WINDOW_FULL;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(kv->fifo.size())) {
+    set_error("oscar_kv_write: needs %lld pages, %zu free", static_cast<long long>(need), kv->fifo.size());
+    return OSCAR_E_NOPAGE;
+  }
+  // ---- commit: allocate pages, update mirrors
+  std::vector<std::pair<int32_t, int32_t>> upd;
+  std::vector<WriteSeq> plan(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    plan[i] = WriteSeq{s, static_cast<int32_t>(kv->len[s]), i, 0};
+    if (kv->len[s] == 0) {
+      const int64_t n2 = std::max<int64_t>(0, n_new - kRing);
+      for (int64_t p = 0; p < ceil_div(n2, kPage); ++p) {
+        const int32_t page = kv->fifo.front();
+        kv->fifo.pop_front();
+        const int32_t idx = static_cast<int32_t>(s * maxp + p);
+        kv->table[idx] = page;
+        upd.emplace_back(idx, page);
+      }
+      kv->n_int2[s] = n2;
+    }
+    kv->len[s] += n_new;
+  }
+  if (kv->plan_only) return OSCAR_OK;
+  hipStream_t st = as_stream(stream);
+  rc = push_table(kv, upd, st);
+  if (rc) return rc;
+  const int n_tiles = static_cast<int>(ceil_div(n_new, kPage));
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    WriteArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.pool = static_cast<uint8_t*>(kv->desc.pool);
+    a.ring = static_cast<uint16_t*>(kv->desc.ring);
+    a.page_table = kv->desc.page_table;
+    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+    a.hkv = kv->desc.num_kv_heads;
+    a.max_pages = kv->desc.max_pages_per_seq;
+    a.n_new = n_new;
+    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
+    hipError_t e = launch_write(a, n_tiles, st);
+    if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
+  }
+  return OSCAR_OK;
+}
+
+int oscar_kv_evict_window(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t n_evict, void* stream) {
+  if (!kv) { set_error("oscar_kv_evict_window: null handle"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (n_evict < 1) { set_error("oscar_kv_evict_window: n_evict must be >= 1"); return OSCAR_E_ARG; }
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  int64_t need = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
+    if (win < n_evict) {
+      set_error("oscar_kv_evict_window: sequence %d holds %lld window tokens < %d", s, static_cast<long long>(win), n_evict);
+      return OSCAR_E_WINDOW_SHORT;
+    }
+    const int64_t p_before = ceil_div(kv->n_int2[s], kPage), p_after = ceil_div(kv->n_int2[s] + n_evict, kPage);
+    if (p_after > maxp) { set_error("oscar_kv_evict_window: sequence %d exceeds max_pages_per_seq", s); return OSCAR_E_NOPAGE; }
+    need += p_after - p_before;
+  }
+  if (need > static_cast<int64_t>(kv->fifo.size())) {
+    set_error("oscar_kv_evict_window: needs %lld pages, %zu free", static_cast<long long>(need), kv->fifo.size());
+    return OSCAR_E_NOPAGE;
+  }
+  std::vector<std::pair<int32_t, int32_t>> upd;
+  std::vector<EvictSeq> plan(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    plan[i] = EvictSeq{s, static_cast<int32_t>(kv->n_int2[s])};
+    const int64_t p_before = ceil_div(kv->n_int2[s], kPage), p_after = ceil_div(kv->n_int2[s] + n_evict, kPage);
+    for (int64_t p = p_before; p < p_after; ++p) {
+      const int32_t page = kv->fifo.front();
+      kv->fifo.pop_front();
+      const int32_t idx = static_cast<int32_t>(s * maxp + p);
+      kv->table[idx] = page;
+      upd.emplace_back(idx, page);
+    }
+    kv->n_int2[s] += n_evict;
+  }
+  if (kv->plan_only) return OSCAR_OK;
+  hipStream_t st = as_stream(stream);
+  rc = push_table(kv, upd, st);
+  if (rc) return rc;
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    EvictArgs a{};
+    a.pool = static_cast<uint8_t*>(kv->desc.pool);
+    a.ring = static_cast<uint16_t*>(kv->desc.ring);
+    a.page_table = kv->desc.page_table;
+    a.hkv = kv->desc.num_kv_heads;
+    a.max_pages = kv->desc.max_pages_per_seq;
+    a.n_evict = n_evict;
+    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
+    hipError_t e = launch_evict(a, st);
+    if (e != hipSuccess) return hip_fail(e, "oscar_kv_evict_window: launch");
+  }
+  return OSCAR_OK;
+}
+
+int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, size_t* bytes) {
+  if (!kv || !bytes) { set_error("oscar_decode_workspace_bytes: null argument"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
+  int64_t max_split = 1;
+  for (int i = 0; i < n_seqs; ++i)
+    max_split = std::max(max_split, ceil_div(ceil_div(kv->n_int2[seq_ids[i]], kPage), pps) + 1);
+  const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
+  *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float);
+  return OSCAR_OK;
+}
+
+int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* q, float sm_scale,
+                      float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) { set_error("oscar_decode_attn: null handle"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (!kv->plan_only && (!q || !out || !ws)) { set_error("oscar_decode_attn: null q, out or workspace"); return OSCAR_E_ARG; }
+  if (!std::isfinite(sm_scale)) { set_error("oscar_decode_attn: non-finite sm_scale"); return OSCAR_E_ARG; }
+  if (!kv->has_rotation) { set_error("oscar_decode_attn: rotation not set"); return OSCAR_E_STATE; }
+  for (int i = 0; i < n_seqs; ++i)
+    if (kv->len[seq_ids[i]] == 0) { set_error("oscar_decode_attn: sequence %d is empty", seq_ids[i]); return OSCAR_E_STATE; }
+  size_t need = 0;
+  rc = oscar_decode_workspace_bytes(kv, seq_ids, n_seqs, &need);
+  if (rc) return rc;
+  if (ws_bytes < need) {
+    set_error("oscar_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
+    return OSCAR_E_WORKSPACE;
+  }
+  if (kv->plan_only) return OSCAR_OK;
+  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
+  hipStream_t st = as_stream(stream);
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.pool = static_cast<const uint8_t*>(kv->desc.pool);
+    a.ring = static_cast<const uint16_t*>(kv->desc.ring);
+    a.page_table = kv->desc.page_table;
+    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+    a.part = static_cast<float*>(ws);
+    a.out = out;
+    a.hkv = kv->desc.num_kv_heads;
+    a.hq = kv->desc.num_q_heads;
+    a.max_pages = kv->desc.max_pages_per_seq;
+    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    a.pages_per_split = static_cast<int32_t>(pps);
+    int64_t max_split = 1;
+    for (int i = 0; i < a.n_seqs; ++i) {
+      const int s = seq_ids[c0 + i];
+      a.seqs[i] = DecodeSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), c0 + i};
+      max_split = std::max(max_split, ceil_div(ceil_div(kv->n_int2[s], kPage), pps) + 1);
+    }
+    a.n_split_max = static_cast<int32_t>(max_split);
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    hipError_t e = launch_decode(a, st);
+    if (e != hipSuccess) return hip_fail(e, "oscar_decode_attn: launch");
+  }
+  return OSCAR_OK;
+}
+
+int oscar_kv_seq_info(const oscar_kv* kv, int32_t seq, int64_t* len, int64_t* n_int2) {
+  if (!kv || seq < 0 || seq >= kv->desc.max_seqs) { set_error("oscar_kv_seq_info: bad handle or seq"); return OSCAR_E_ARG; }
+  if (len) *len = kv->len[seq];
+  if (n_int2) *n_int2 = kv->n_int2[seq];
+  return OSCAR_OK;
+}
+
+int oscar_kv_get_page_table(const oscar_kv* kv, int32_t* host_out) {
+  if (!kv || !host_out) { set_error("oscar_kv_get_page_table: null argument"); return OSCAR_E_ARG; }
+  std::memcpy(host_out, kv->table.data(), kv->table.size() * sizeof(int32_t));
+  return OSCAR_OK;
+}
+
+int oscar_kv_free_pages(const oscar_kv* kv, int32_t* count, int32_t* host_out) {
+  if (!kv) { set_error("oscar_kv_free_pages: null handle"); return OSCAR_E_ARG; }
+  if (count) *count = static_cast<int32_t>(kv->fifo.size());
+  if (host_out) std::copy(kv->fifo.begin(), kv->fifo.end(), host_out);
+  return OSCAR_OK;
+}
+
+int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, void* stream) {
+  if (!kv || seq < 0 || seq >= kv->desc.max_seqs) { set_error("oscar_kv_reset_seq: bad handle or seq"); return OSCAR_E_ARG; }
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  const int64_t pages = ceil_div(kv->n_int2[seq], kPage);
+  std::vector<std::pair<int32_t, int32_t>> upd;
+  for (int64_t p = 0; p < pages; ++p) {
+    const int32_t idx = static_cast<int32_t>(seq * maxp + p);
+    kv->fifo.push_back(kv->table[idx]);
+    kv->table[idx] = -1;
+    upd.emplace_back(idx, -1);
+  }
+  kv->len[seq] = 0;
+  kv->n_int2[seq] = 0;
+  return push_table(kv, upd, as_stream(stream));
+}
+
+int oscar_kv_set_decode_split(oscar_kv* kv, int32_t pages_per_split) {
+  if (!kv || pages_per_split < 0) { set_error("oscar_kv_set_decode_split: bad argument"); return OSCAR_E_ARG; }
+  kv->pages_per_split = pages_per_split;
+  return OSCAR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,246 @@
+/*
+ * oscar.h - C ABI of liboscar: an INT2 paged KV cache with a BF16 attention-sink
+ * region and a BF16 recent window, its write path, its window-eviction
+ * requantizer and a fused split-K GQA decode-attention read path, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources (public pages describing OSCAR, "Offline Spectral Covariance-Aware
+ * Rotation"):
+ *   [A] axbrief, "Together AI's OSCAR breaks the 2-bit KV cache accuracy
+ *       barrier" - sections "Together AI, INT2 KV 캐시 시스템 'OSCAR' 공개"
+ *       (mixed-precision paged INT2 cache, BF16 sink + recent window, 0.24 %
+ *       BF16 at 128K) and "어텐션 통계 기반 회전과 Triton 커널의 결합"
+ *       (R_K = U_Q H P_br from the query covariance, clipping c_K = 0.96 /
+ *       c_V = 0.92, per-token asymmetric INT2 with 64-channel groups, one
+ *       fused read pass: unpack, dequantize, undo rotation, attend; R_V folded
+ *       into the projection weights offline).
+ *   [B] techllm, "KV cache compression: TurboQuant, OSCAR, EpiCache" - section
+ *       "OSCAR — INT2를 실전으로 끌어내린 캘리브레이션 회전" (Hadamard +
+ *       bit-reversal spread, recent tokens BF16 / old history INT2).
+ *
+ * Conventions shared by every call
+ *   - Row vectors: a key k is stored rotated as k' = k . R_K; the decode query
+ *     is rotated the same way (q' = q . R_K), which gives the same scores as
+ *     undoing the rotation on every key ([A], rotation section) because R_K is
+ *     orthogonal.
+ *   - Values arrive already rotated by R_V ([A]: R_V is absorbed into the value
+ *     and output projections offline) and are stored as given; outputs are in
+ *     that same basis.
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - Device pointers are plain HIP device addresses; streams are hipStream_t
+ *     passed as void* (NULL = the default stream).  Every device action is
+ *     enqueued on that stream in call order; no call synchronizes the device.
+ *   - The caller owns every device buffer (pool, ring, page table, rotation,
+ *     workspace, inputs, outputs) and keeps it alive until the stream has
+ *     passed the call.  The library allocates host memory only (the handle
+ *     and its mirror of the page table), never device memory.
+ *   - Errors: every call returns OSCAR_OK (0) or a negative status.  A call
+ *     that fails validation changes nothing; oscar_last_error() returns a
+ *     message for the calling thread.  OSCAR_E_HIP (a launch failure) leaves
+ *     the store undefined.  Faults inside kernels surface at the caller's next
+ *     synchronization.
+ *   - One handle must not be used from two host threads at once.
+ *
+ * Fixed shape (the workloads' and the pages' parameters):
+ *   head_dim 128, channel group 64, 64 tokens per page, 64 sink tokens,
+ *   256-token recent window, c_K = 0.96, c_V = 0.92.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_HEAD_DIM        128
+#define OSCAR_GROUP           64
+#define OSCAR_PAGE_TOKENS     64
+#define OSCAR_SINK_TOKENS     64
+#define OSCAR_WINDOW_TOKENS   256
+#define OSCAR_RING_SLOTS      (OSCAR_SINK_TOKENS + OSCAR_WINDOW_TOKENS)
+#define OSCAR_HEAD_BLOCK      5120   /* bytes of one KV head in one page */
+#define OSCAR_ROT_HEAD_BYTES  163840 /* bytes of one KV head's rotation block */
+#define OSCAR_MAX_GQA         8      /* Hq / Hkv must be 1, 2, 4 or 8 */
+
+enum {
+    OSCAR_OK = 0,
+    OSCAR_E_ARG = -1,           /* bad argument: null pointer, shape, range, duplicate seq id */
+    OSCAR_E_NOPAGE = -2,        /* the free-page FIFO cannot supply every page the call needs */
+    OSCAR_E_WINDOW_FULL = -3,   /* an append would hold more than 256 window tokens */
+    OSCAR_E_WINDOW_SHORT = -4,  /* eviction asks for more tokens than the window holds */
+    OSCAR_E_NUMERIC = -5,       /* non-finite calibration input or eigensolver failure */
+    OSCAR_E_HIP = -6,           /* a HIP runtime call or kernel launch failed */
+    OSCAR_E_WORKSPACE = -7,     /* decode workspace smaller than oscar_decode_workspace_bytes */
+    OSCAR_E_STATE = -8          /* the call does not fit the sequence's state (e.g. empty sequence) */
+};
+
+/* Set in oscar_kv_desc.flags: keep every piece of host bookkeeping (page table
+ * mirror, FIFO, lengths) but enqueue no device work and accept NULL device
+ * pointers.  For capacity planning and for testing the allocator on a host
+ * without a GPU. */
+#define OSCAR_FLAG_PLAN_ONLY 1
+
+typedef struct oscar_kv oscar_kv;
+
+/*
+ * One attention layer's mixed-precision paged store ([A] Release section: the
+ * INT2 cache stays a paged-attention cache, BF16 sink + recent window, INT2
+ * history).
+ *
+ * pool        device, num_pages * num_kv_heads * OSCAR_HEAD_BLOCK bytes.  Page p,
+ *             KV head h is the 5120-byte block at (p * num_kv_heads + h) * 5120:
+ *               [   0, 2048) key codes, [2048, 4096) value codes: 2 bits per code,
+ *                            512 little-endian 32-bit words each;
+ *               [4096, 5120) metadata, 16 bytes per token j at 4096 + 16 j:
+ *                            fp16 {sK0, loK0, sK1, loK1, sV0, loV0, sV1, loV1}
+ *                            (scale and minimum of channel groups 0-63, 64-127).
+ *             Key code of token j, channel c:
+ *               t = j/16, n = j%16, g = c/64, kq = (c%64)/16, u = c%16,
+ *               word = 256*(t/2) + 4*(16*kq + n) + 2*(t%2) + g,
+ *               bit  = 8*(u%4) + 2*(u/4).
+ *             Value code of token j, channel c:
+ *               ct = c/16, n = c%16, s = j/32, kq = (j%32)/8, kk = j%8,
+ *               word = 256*(ct/4) + 4*(16*kq + n) + ct%4,
+ *               bit  = 2*(4*s + kk/2) + 16*(kk%2).
+ *             Slots of tokens not yet written in a page are zero.
+ * ring        device bf16, [max_seqs][num_kv_heads][2 (K,V)][320][128].  Slot p < 64
+ *             holds sink position p; window position p >= 64 sits in slot
+ *             64 + (p - 64) % 256.  Keys are stored rotated (bf16 of k . R_K).
+ * page_table  device int32 [max_seqs][max_pages_per_seq]: physical page of each
+ *             64-token INT2 page, -1 where none.  INT2 index i (position 64 + i)
+ *             lives in page page_table[seq][i / 64], slot i % 64.
+ * rot         device, num_kv_heads * OSCAR_ROT_HEAD_BYTES bytes, written by
+ *             oscar_kv_set_rotation: per KV head R_K fp32 [128][128] followed by
+ *             three bf16 [128][128] terms whose sum is R_K to fp32 precision.
+ */
+typedef struct {
+    int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads with Hq/Hkv <= 8 */
+    int32_t num_kv_heads;       /* Hkv >= 1 */
+    int32_t max_seqs;           /* sequence slots; seq ids are 0 .. max_seqs-1 */
+    int32_t max_pages_per_seq;  /* page-table row length */
+    int32_t num_pages;          /* pages in the pool */
+    int32_t flags;              /* 0 or OSCAR_FLAG_PLAN_ONLY */
+    void *pool;
+    void *ring;
+    int32_t *page_table;
+    void *rot;
+} oscar_kv_desc;
+
+/*
+ * Key rotation from calibration queries, on the host, in fp64 ([A] rotation
+ * section: R_K = U_Q . H_Had . P_br, U_Q the eigenvectors of the query
+ * covariance C_Q = (1/N) sum_n q_n^T q_n; [B]: Hadamard + bit reversal).
+ *
+ * q        host fp32 [n][d], row n is one query (pool every query head that
+ *          reads the KV head).  No mean is subtracted.
+ * d        must be 128.
+ * rot_out  host fp32 [d][d], row-major, R_K = U . H . P with U's columns in
+ *          descending eigenvalue order, each column's largest-magnitude entry
+ *          positive, H the Sylvester Hadamard matrix / sqrt(d), and
+ *          (x . P)_j = x_{bitreverse(j)}.
+ * eig_out  host fp64 [d], descending eigenvalues of C_Q, or NULL.
+ * Errors: OSCAR_E_ARG (null pointer, n < 1, d != 128), OSCAR_E_NUMERIC
+ * (non-finite input, eigensolver did not converge).  Writes nothing on error.
+ */
+int oscar_calibrate_host(const float *q, int64_t n, int32_t d, float *rot_out, double *eig_out);
+
+/* Bytes the caller must allocate for each device buffer of a store with this
+ * descriptor (device pointers in desc are ignored).  Any output may be NULL. */
+int oscar_kv_buffer_bytes(const oscar_kv_desc *desc, size_t *pool, size_t *ring,
+                          size_t *page_table, size_t *rot);
+
+/*
+ * Create a store.  free_pages (host, n_free entries, distinct, each in
+ * [0, num_pages)) is the initial FIFO of free physical pages.  Unless
+ * OSCAR_FLAG_PLAN_ONLY is set, fills the device page table with -1 on stream.
+ * Every sequence starts empty.  *out is set only on success.
+ */
+int oscar_kv_create(const oscar_kv_desc *desc, const int32_t *free_pages, int32_t n_free,
+                    void *stream, oscar_kv **out);
+
+/*
+ * Upload R_K for every KV head (host fp32 [num_kv_heads][128][128], row-major,
+ * as produced by oscar_calibrate_host) into desc.rot on stream, with its bf16
+ * three-term split.  Must be called before the first write or decode.
+ * Errors: OSCAR_E_ARG (null), OSCAR_E_NUMERIC (non-finite entry).
+ */
+int oscar_kv_set_rotation(oscar_kv *kv, const float *rot_host, void *stream);
+
+/*
+ * Append n_new tokens to each listed sequence ([A] rotation section: each new
+ * key is rotated by R_K, clipped with c_K, quantized per token to asymmetric
+ * INT2 in 64-channel groups; values likewise with c_V, unrotated).
+ *
+ * seq_ids  host int32 [n_seqs], distinct.
+ * k, v     device bf16 [n_seqs][n_new][num_kv_heads][128], token order = position
+ *          order.
+ * Routing: into an empty sequence of final length L, positions < 64 go to the
+ * BF16 sink, positions 64 .. L-257 are quantized straight to INT2 (from the
+ * fp32 rotated key) and the last min(L-64, 256) positions go to the BF16
+ * window.  Into a non-empty sequence, positions < 64 go to the sink and the
+ * rest to the window.  Pages are taken from the FIFO in seq_ids order,
+ * ascending within a sequence.
+ * Errors: OSCAR_E_ARG, OSCAR_E_WINDOW_FULL (a non-empty sequence's window
+ * would exceed 256 tokens: evict first), OSCAR_E_NOPAGE (FIFO too short or a
+ * sequence would exceed max_pages_per_seq).
+ */
+int oscar_kv_write(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t n_new,
+                   const void *k, const void *v, void *stream);
+
+/*
+ * Move the n_evict oldest window tokens of each listed sequence into INT2
+ * ([A]/[B]: old history is INT2, recent tokens BF16): each is quantized from
+ * its stored bf16 key (already rotated) and value, into INT2 index n_int2,
+ * n_int2 + 1, ...; a page is taken from the FIFO whenever the index is a
+ * multiple of 64 (sequences in seq_ids order).
+ * Errors: OSCAR_E_ARG, OSCAR_E_WINDOW_SHORT, OSCAR_E_NOPAGE.
+ */
+int oscar_kv_evict_window(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t n_evict,
+                          void *stream);
+
+/* Device workspace bytes oscar_decode_attn needs for these sequences in their
+ * current state (split-K partials). */
+int oscar_decode_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs,
+                                 size_t *bytes);
+
+/*
+ * One decode step of GQA attention for each listed sequence over everything
+ * it stores ([A] rotation section: one fused pass unpacks, dequantizes,
+ * handles the rotation and attends, with no extra memory traffic).
+ *
+ * q         device bf16 [n_seqs][num_q_heads][128] (unrotated queries).
+ * sm_scale  softmax scale (1/sqrt(128) for standard attention).
+ * out       device fp32 [n_seqs][num_q_heads][128], softmax(sm_scale q k^T) v in
+ *           the R_V basis.
+ * ws        device workspace of at least oscar_decode_workspace_bytes bytes.
+ * Errors: OSCAR_E_ARG, OSCAR_E_STATE (an empty sequence), OSCAR_E_WORKSPACE.
+ */
+int oscar_decode_attn(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *q,
+                      float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Length and INT2 token count of one sequence. */
+int oscar_kv_seq_info(const oscar_kv *kv, int32_t seq, int64_t *len, int64_t *n_int2);
+
+/* Copy of the host mirror of the page table, int32 [max_seqs][max_pages_per_seq]. */
+int oscar_kv_get_page_table(const oscar_kv *kv, int32_t *host_out);
+
+/* Number of free pages and the FIFO contents (host int32, may be NULL). */
+int oscar_kv_free_pages(const oscar_kv *kv, int32_t *count, int32_t *host_out);
+
+/* Empty one sequence: its pages go to the FIFO tail in ascending logical order;
+ * its device page-table row is reset to -1 on stream. */
+int oscar_kv_reset_seq(oscar_kv *kv, int32_t seq, void *stream);
+
+/* Decode tuning: pages_per_split = 0 picks a split size from the batch. */
+int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);
+
+const char *oscar_last_error(void);
+void oscar_kv_destroy(oscar_kv *kv);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_H */

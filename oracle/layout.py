@@ -69,12 +69,25 @@ def v_code_position(j, c):
     return word, bit
 
 
-def _pack_area(codes, position) -> np.ndarray:
-    jj, cc = np.meshgrid(np.arange(codes.shape[0]), np.arange(HEAD_DIM), indexing="ij")
+def _positions_sorted(position):
+    """(order, bits) so that codes.ravel()[order].reshape(512, 16) groups the 16 codes of each word."""
+    jj, cc = np.meshgrid(np.arange(PAGE_TOKENS), np.arange(HEAD_DIM), indexing="ij")
     word, bit = position(jj, cc)
-    words = np.zeros(512, dtype=np.uint64)
-    np.add.at(words, word.ravel(), codes.astype(np.uint64).ravel() << bit.ravel().astype(np.uint64))
-    return words.astype(np.uint32).view(np.uint8)
+    key = (word * 32 + bit).ravel()
+    order = np.argsort(key, kind="stable")
+    return order, bit.ravel()[order].reshape(512, 16).astype(np.uint32)
+
+
+_SORTED = {}
+
+
+def _pack_area(codes, position) -> np.ndarray:
+    if position not in _SORTED:
+        _SORTED[position] = _positions_sorted(position)
+    order, bits = _SORTED[position]
+    c = np.asarray(codes, dtype=np.uint32).ravel()[order].reshape(512, 16)
+    words = np.bitwise_or.reduce(c << bits, axis=1).astype(np.uint32)
+    return words.view(np.uint8)
 
 
 def _unpack_area(area, n_tokens, position) -> np.ndarray:

@@ -142,7 +142,7 @@ class OracleStore:
         for b, s in enumerate(seq_ids):
             L0 = int(self.length[s])
             k64 = bf16_to_f64(k_bits[b])                          # [n_new, Hkv, d]
-            x = np.einsum("thi,hij->thj", k64, self.rot)          # k . R_K per head, fp64
+            x = np.matmul(k64.transpose(1, 0, 2), self.rot).transpose(1, 0, 2)   # k . R_K per head, fp64
             kx_bf = to_bf16_bits_f64(x)
             if L0 == 0:
                 L = n_new

@@ -65,9 +65,11 @@ def haar(n: int, rng: np.random.Generator) -> np.ndarray:
 
 def f32_to_bf16_bits(x) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
-    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+    r = (b >> np.uint32(16)) & np.uint32(1)      # finite inputs: the sum below cannot wrap
+    r += np.uint32(0x7FFF)
+    r += b
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits) -> np.ndarray:
@@ -129,7 +131,6 @@ def ragged_lengths(cfg: int, n: int, lo: int, hi: int) -> np.ndarray:
 # ----------------------------------------------------------------------------- counter-based bulk draw
 
 _M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)
-_W0, _W1 = np.uint64(0x9E3779B9), np.uint64(0xBB67AE85)
 _MASK32 = np.uint64(0xFFFFFFFF)
 # sqrt(3) / 65536 rounded to fp32: unit variance for the centred sum of four 16-bit uniforms.
 IH4_SCALE = np.float32(np.sqrt(3.0) / 65536.0)
@@ -137,19 +138,28 @@ IH4_CENTER = 131070  # 4 * 32767.5, rounded down; the draw is centred to within 
 
 
 def philox4x32_10(c0, c1, c2, c3, k0, k1):
-    """Philox4x32 with 10 rounds on uint32-valued arrays (held in uint64)."""
+    """Philox4x32 with 10 rounds on uint32-valued arrays; returns four uint64 arrays of 32-bit words."""
     c0, c1, c2, c3 = (np.asarray(c, dtype=np.uint64) & _MASK32 for c in (c0, c1, c2, c3))
-    k0 = np.uint64(int(k0) & 0xFFFFFFFF)
-    k1 = np.uint64(int(k1) & 0xFFFFFFFF)
+    k0 = int(k0) & 0xFFFFFFFF
+    k1 = int(k1) & 0xFFFFFFFF
+    s32 = np.uint64(32)
+    p0 = np.empty_like(c0)
+    p1 = np.empty_like(c0)
     for r in range(10):
-        p0 = _M0 * c0
-        p1 = _M1 * c2
-        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
-        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
-        c0, c1, c2, c3 = (hi1 ^ c1 ^ k0) & _MASK32, lo1, (hi0 ^ c3 ^ k1) & _MASK32, lo0
-        if r < 9:
-            k0 = (k0 + _W0) & _MASK32
-            k1 = (k1 + _W1) & _MASK32
+        np.multiply(c0, _M0, out=p0)
+        np.multiply(c2, _M1, out=p1)
+        # new c0 = hi(p1) ^ c1 ^ k0 ; c1 = lo(p1) ; c2 = hi(p0) ^ c3 ^ k1 ; c3 = lo(p0)
+        n0 = p1 >> s32
+        n0 ^= c1
+        n0 ^= np.uint64(k0)
+        n2 = p0 >> s32
+        n2 ^= c3
+        n2 ^= np.uint64(k1)
+        c1 = p1 & _MASK32
+        c3 = p0 & _MASK32
+        c0, c2 = n0, n2
+        k0 = (k0 + 0x9E3779B9) & 0xFFFFFFFF
+        k1 = (k1 + 0xBB67AE85) & 0xFFFFFFFF
     return c0, c1, c2, c3
 
 

@@ -1,0 +1,134 @@
+"""CPU tests of the C-ABI library: exports, host calibration, allocator/bookkeeping (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_write_amd as oscar
+import synth
+from oracle import calibration, store as ostore
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = oscar.load()
+    names = _header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(oscar.EXPORTS)
+
+
+def test_calibrate_host_matches_oracle():
+    for kv in range(2):
+        qb = synth.calibration_queries(synth.CFG_QWEN3_4B, 0, kv)
+        q = synth.bf16_bits_to_f32(qb)
+        rot, eig = oscar.oscar_calibrate_host(q)
+        r_ref, w_ref = calibration.key_rotation(q.astype(np.float64))
+        assert np.abs(eig - w_ref).max() < 1e-12 * w_ref[0]
+        # eigenvectors of close eigenvalues are determined to ~eps*|C|/gap; compare per column
+        u = rot.astype(np.float64) @ calibration.bit_reversal_matrix(128).T @ calibration.sylvester_hadamard(128)
+        u_ref = r_ref @ calibration.bit_reversal_matrix(128).T @ calibration.sylvester_hadamard(128)
+        gaps = np.minimum(np.abs(np.diff(w_ref, prepend=np.inf)), np.abs(np.diff(w_ref, append=-np.inf)))
+        col_err = np.abs(u - u_ref).max(axis=0)
+        assert np.all(col_err <= 2e-7 + 1e-14 * w_ref[0] / gaps * 100), col_err.max()
+        assert np.abs(rot - r_ref.astype(np.float32)).max() < 1e-5
+        r64 = rot.astype(np.float64)
+        assert np.abs(r64.T @ r64 - np.eye(128)).max() < 2e-6
+
+
+def test_calibrate_host_errors():
+    q = np.ones((4, 128), np.float32)
+    q[1, 3] = np.nan
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_calibrate_host(q)
+    assert e.value.status == oscar.E_NUMERIC
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_calibrate_host(np.ones((4, 64), np.float32))
+    assert e.value.status == oscar.E_ARG
+
+
+def _plan_store(hkv=2, hq=8, max_seqs=4, max_pages=8, num_pages=12, free=None):
+    s = oscar.KVStore(hq, hkv, max_seqs, max_pages, num_pages, free_pages=free, plan_only=True)
+    s.set_rotation(np.stack([np.eye(128, dtype=np.float32)] * hkv))
+    return s
+
+
+def _oracle_store(hkv=2, max_seqs=4, max_pages=8, num_pages=12, free=None):
+    free = list(range(num_pages)) if free is None else list(free)
+    return ostore.OracleStore(hkv, max_seqs, max_pages, num_pages, free,
+                              np.stack([np.eye(128, dtype=np.float32)] * hkv))
+
+
+def test_plan_only_allocator_matches_oracle():
+    free = np.random.default_rng(0).permutation(12).astype(np.int32)
+    lib_s = _plan_store(free=free)
+    ora = _oracle_store(free=free)
+    zeros = lambda n_seqs, n: np.zeros((n_seqs, n, 2, 128), np.uint16)  # noqa: E731
+    ops = [("w", [2, 0], 320 + 70), ("e", [0, 2], 58), ("e", [2], 1), ("w", [1], 200),
+           ("w", [0, 2], 1), ("e", [0], 64), ("w", [3], 500)]
+    for op, ids, n in ops:
+        if op == "w":
+            lib_s.write(ids, None, None, n_new=n)
+            ora.write(ids, zeros(len(ids), n), zeros(len(ids), n))
+        else:
+            lib_s.evict(ids, n)
+            ora.evict(ids, n)
+        assert np.array_equal(lib_s.page_table(), ora.page_table), (op, ids, n)
+        assert list(lib_s.free_pages()) == list(ora.free)
+        for s in range(4):
+            assert lib_s.seq_info(s) == (ora.length[s], ora.n_int2[s])
+    lib_s.reset_seq(2)
+    ora.reset_seq(2)
+    assert np.array_equal(lib_s.page_table(), ora.page_table)
+    assert list(lib_s.free_pages()) == list(ora.free)
+
+
+def test_errors_leave_state_unchanged():
+    s = _plan_store(num_pages=6, max_pages=4)
+    s.write([0], None, None, n_new=320 + 128)      # 2 pages
+    snap = (s.page_table().copy(), list(s.free_pages()), s.seq_info(0))
+
+    def unchanged():
+        assert np.array_equal(s.page_table(), snap[0]) and list(s.free_pages()) == snap[1]
+        assert s.seq_info(0) == snap[2]
+
+    cases = [
+        (lambda: s.write([0], None, None, n_new=1), oscar.E_WINDOW_FULL),
+        (lambda: s.evict([0], 257), oscar.E_WINDOW_SHORT),
+        (lambda: s.evict([1], 1), oscar.E_WINDOW_SHORT),
+        (lambda: s.write([1, 2], None, None, n_new=320 + 64 * 3), oscar.E_NOPAGE),
+        (lambda: s.write([1], None, None, n_new=320 + 64 * 5), oscar.E_NOPAGE),   # > max_pages_per_seq
+        (lambda: s.write([0, 0], None, None, n_new=1), oscar.E_ARG),
+        (lambda: s.write([9], None, None, n_new=1), oscar.E_ARG),
+        (lambda: s.evict([0], 0), oscar.E_ARG),
+    ]
+    for fn, status in cases:
+        with pytest.raises(oscar.OscarError) as e:
+            fn()
+        assert e.value.status == status
+        unchanged()
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_decode_attn(s, [1], None, 0.1, None, None)
+    assert e.value.status == oscar.E_STATE
+
+
+def test_workspace_bytes_and_split_choice():
+    s = _plan_store(max_pages=64, num_pages=64)
+    s.write([0], None, None, n_new=320 + 64 * 20)
+    s.write([1], None, None, n_new=100)
+    nb = s.workspace_bytes([0, 1])
+    assert nb > 0 and nb % (130 * 4) == 0
+    s.set_decode_split(4)
+    nb4 = s.workspace_bytes([0, 1])
+    # 20 pages / 4 per split = 5 INT2 splits + 1 BF16 split, 2 seqs x 8 q heads
+    assert nb4 == 2 * 8 * 6 * 130 * 4
