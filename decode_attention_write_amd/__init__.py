@@ -36,7 +36,7 @@ EXPORTS = [
     "oscar_calibrate_host", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
-    "oscar_kv_set_decode_split", "oscar_last_error", "oscar_kv_destroy",
+    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_last_error", "oscar_kv_destroy",
 ]
 
 
@@ -80,6 +80,7 @@ def load():
         "oscar_kv_free_pages": [P, P, P],
         "oscar_kv_reset_seq": [P, I32, P],
         "oscar_kv_set_decode_split": [P, I32],
+        "oscar_kv_set_decode_kernel": [P, I32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -249,6 +250,10 @@ class KVStore:
 
     def set_decode_split(self, pages_per_split):
         _check(load().oscar_kv_set_decode_split(self.handle, int(pages_per_split)))
+
+    def set_decode_kernel(self, kernel):
+        """0 = matrix-core kernel (default), 1 = reference-grade fp32 kernel."""
+        _check(load().oscar_kv_set_decode_kernel(self.handle, int(kernel)))
 
     # ---- views of the device buffers (for tests and export)
     def pool_view(self):

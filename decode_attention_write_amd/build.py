@@ -28,6 +28,7 @@ SOURCES = {
     "calibrate.cpp": [],
     "write.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "decode_mfma.hip": [],
 }
 
 

@@ -203,7 +203,12 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a) {
   a.out[(static_cast<size_t>(sq.src) * a.hq + h) * D + c] = O / L;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.n_split_max, a.hkv, a.n_seqs);
   const int gqa = a.hq / a.hkv;
   switch (gqa) {
@@ -213,9 +218,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     case 8: hipLaunchKernelGGL(k_decode_simple<8>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

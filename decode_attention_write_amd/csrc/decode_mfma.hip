@@ -1,0 +1,468 @@
+// Fused INT2 decode attention on the gfx950 matrix cores.
+//
+// Method: axbrief, "Together AI's OSCAR breaks the 2-bit KV cache accuracy
+// barrier", section "어텐션 통계 기반 회전과 Triton 커널의 결합" - the read path
+// unpacks the INT2 bytes, dequantizes, handles the rotation and attends in one
+// pass without extra memory traffic.  Here the rotation is applied once to the
+// query (q' = q R_K; scores are unchanged because R_K is orthogonal) and the
+// dequantization is folded into the matrix products:
+//
+//   score_j = sum_g s_jg (q'_g . c_jg) + lo_jg sum(q'_g)
+//   out     = sum_j p_j (lo_jg + s_jg c_j) = sum_j p_j lo_jg + sum_j (p_j s_jg) c_j
+//
+// so both products run on the raw 2-bit codes:
+//   * Q.K: i8 MFMA 16x16x64.  q' is split into two int8 terms (q' ~ sigma (t1 + t2/128),
+//     error <= sigma/256) and the 16 A rows are (term, group, head): one instruction
+//     per (16-token tile, channel group) covers 4 heads, both terms and both groups;
+//     accumulation is exact integer arithmetic.  The rows are merged across lanes
+//     with permlane swaps so that afterwards lane = token, register = head.
+//   * P.V: f16 MFMA 16x16x32.  A value code c placed in mantissa bits e..e+1 of an
+//     f16 with zero exponent *is* the f16 denormal c * 2^(e-24); one mask gives two
+//     such operands per 32-bit word.  The per-position factor is folded into P
+//     (A operand = p * s * 2^(4-e), at most 65504 since p <= 1), so the product is
+//     exactly p s c 2^-20.  P is carried as an fp16 pair hi + lo (lo = the rounding
+//     residual), which keeps 22 bits of p * s: the output is a strongly cancelling
+//     sum, and a single fp16 P costs ~5e-4 relative error.  With GQA <= 4 the lo rows
+//     ride in the otherwise empty rows 8..15 of the same instruction.
+// Each wavefront walks the pages of one (sequence, KV head, split) with 128-bit loads
+// of the raw page block, keeps a running softmax max (rescaling only when a new max
+// appears), and writes an (m, l, o) partial for the split combine.
+#include "common.h"
+
+namespace oscar {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ workspace layout
+// Per (sequence of the chunk, KV head): prepared query operands.
+constexpr int QP_AOPS = 0;        // int8 A operands: [head block][lane][K-step][16 B] = 2 x 64 x 32 B
+constexpr int QP_QF = 4096;       // fp32 q' (scaled to log2 units) [head][128]
+constexpr int QP_CONST = 8192;    // fp32 per head: c_h = sigma_h / 128, Qt0'' , Qt1''
+constexpr int QP_STRIDE = QPREP_STRIDE;
+
+__host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
+  return static_cast<size_t>(a.n_seqs) * a.hq * a.n_split_max * PART_STRIDE * sizeof(float);
+}
+
+// ------------------------------------------------------------------ query preparation
+// Grid (KV heads, sequences of the chunk), 256 threads.
+template <int G>
+__global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
+  const int kvh = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x;
+  const DecodeSeq sq = a.seqs[sl];
+  __shared__ float qf[G][D];
+  __shared__ float sig[G];
+  __shared__ float qt[G][2];
+  const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
+  const uint16_t* q = a.q + (static_cast<size_t>(sq.src) * a.hq + static_cast<size_t>(kvh) * G) * D;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(a.part) + qprep_offset(a) + (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, c = idx % D;
+    float acc = 0.0f;
+    for (int i = 0; i < D; ++i) acc = fmaf(bf16_to_f32(q[h * D + i]), rot[i * D + c], acc);
+    qf[h][c] = acc * a.scale_log2;
+  }
+  __syncthreads();
+  for (int h = tid >> 6; h < G; h += 4) {
+    // one wave per head: sigma = max|q'| / 127, per-group sums
+    const int l = tid & 63;
+    float mx = fmaxf(fabsf(qf[h][l]), fabsf(qf[h][l + 64]));
+    float s0 = qf[h][l], s1 = qf[h][l + 64];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      s0 += __shfl_xor(s0, off, 64);
+      s1 += __shfl_xor(s1, off, 64);
+    }
+    if (l == 0) {
+      sig[h] = (mx > 0.0f) ? mx / 127.0f : 1.0f;
+      qt[h][0] = s0;
+      qt[h][1] = s1;
+    }
+  }
+  __syncthreads();
+  float* wf = reinterpret_cast<float*>(ws + QP_QF);
+  for (int idx = tid; idx < G * D; idx += 256) wf[idx] = qf[idx / D][idx % D];
+  float* wc = reinterpret_cast<float*>(ws + QP_CONST);
+  if (tid < G) {
+    wc[3 * tid + 0] = sig[tid] / 128.0f;
+    wc[3 * tid + 1] = qt[tid][0] * 128.0f / sig[tid];
+    wc[3 * tid + 2] = qt[tid][1] * 128.0f / sig[tid];
+  }
+  // A operands: head block hb, lane l: row m = l % 16 = 4 (2 tau + grp) + h4, K-step g covers
+  // channels 64 g + 16 (l / 16) + j, j = 0..15 (byte j of the lane's 16 bytes)
+  constexpr int HB = (G + 3) / 4;
+  int8_t* wa = reinterpret_cast<int8_t*>(ws + QP_AOPS);
+  for (int idx = tid; idx < HB * 64 * 2 * 16; idx += 256) {
+    const int j = idx & 15, g = (idx >> 4) & 1, l = (idx >> 5) & 63, hb = idx >> 11;
+    const int m = l & 15, tau = m >> 3, grp = (m >> 2) & 1, h = 4 * hb + (m & 3);
+    int8_t v = 0;
+    if (grp == g && h < G) {
+      const int c = 64 * g + 16 * (l >> 4) + j;
+      const float x = qf[h][c] / sig[h];
+      const float t1 = rintf(x);
+      v = static_cast<int8_t>(tau == 0 ? t1 : rintf((x - t1) * 128.0f));
+    }
+    wa[idx] = v;
+  }
+}
+
+// ------------------------------------------------------------------ helpers
+
+__device__ inline float lane_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ inline float lane_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  v4u u = {a, b, c, d};
+  return __builtin_bit_cast(v8h, u);
+}
+
+// Exponent e of the f16 denormal a value code lands in, by its position p' = 4 s + kk/2
+// within the 32-bit word (see the unpack in the page loop).
+__device__ inline int vcode_exp(int p) {
+  constexpr int E[8] = {4, 6, 4, 6, 8, 4, 6, 8};
+  return E[p];
+}
+
+// ------------------------------------------------------------------ BF16 sink + window split
+// One wavefront: lane = ring slot for the scores, lane = channel pair for the value product.
+template <int G>
+__device__ void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, const float* qf,
+                           float (*pbuf)[64]) {
+  const int lane = threadIdx.x;
+  const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
+  const int n_win = max(0, sq.len - SINK - sq.n_int2);
+  float m[G], l[G], o0[G], o1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.0f; o0[h] = 0.0f; o1[h] = 0.0f; }
+  for (int ch = 0; ch < RING / 64; ++ch) {
+    const int slot = ch * 64 + lane;
+    const bool ok = (slot < SINK) ? (slot < min(sq.len, SINK))
+                                  : (((slot - SINK - (sq.n_int2 % WIN) + WIN) % WIN) < n_win);
+    if (!__any(ok)) continue;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.0f;
+    if (ok) {
+      const uint4* kr = reinterpret_cast<const uint4*>(a.ring + ring_head + static_cast<size_t>(slot) * D);
+#pragma unroll 4
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const uint4 w = kr[c8];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float k0 = __uint_as_float(ww[e] << 16), k1 = __uint_as_float(ww[e] & 0xFFFF0000u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[h] = fmaf(qf[h * D + 8 * c8 + 2 * e + 1], k1, fmaf(qf[h * D + 8 * c8 + 2 * e], k0, s[h]));
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sc = ok ? s[h] : -INFINITY;
+      const float mn = fmaxf(m[h], lane_max(sc));
+      const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - mn);
+      const float p = ok ? exp2f(sc - mn) : 0.0f;
+      l[h] = l[h] * alpha + lane_sum(p);
+      o0[h] *= alpha;
+      o1[h] *= alpha;
+      m[h] = mn;
+      pbuf[h][lane] = p;
+    }
+    __syncthreads();
+    // value product: lane owns channels 2 lane, 2 lane + 1
+    for (int j = 0; j < 64; ++j) {
+      const int sj = ch * 64 + j;
+      const bool okj = (sj < SINK) ? (sj < min(sq.len, SINK))
+                                   : (((sj - SINK - (sq.n_int2 % WIN) + WIN) % WIN) < n_win);
+      if (!okj) continue;  // uniform across the wave
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(a.ring + ring_head + static_cast<size_t>(RING + sj) * D + 2 * lane);
+      const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        o0[h] = fmaf(pbuf[h][j], v0, o0[h]);
+        o1[h] = fmaf(pbuf[h][j], v1, o1[h]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* rec = a.part + ((static_cast<size_t>(sl) * a.hq + kvh * G + h) * a.n_split_max + split) * PART_STRIDE;
+    if (lane == 0) { rec[0] = m[h]; rec[1] = l[h]; }
+    rec[2 + 2 * lane] = o0[h];
+    rec[3 + 2 * lane] = o1[h];
+  }
+}
+
+// ------------------------------------------------------------------ INT2 page loop
+// Grid (splits, KV heads, sequences of the chunk), one wavefront per work-group.
+// Split n_isplits (the last one) is the BF16 sink + window work.
+
+template <int G>
+__global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
+  constexpr int GP = G < 4 ? 4 : G;       // heads padded to a multiple of 4
+  constexpr int HB = GP / 4;              // head blocks (MFMA row blocks of Q.K)
+  const int split = blockIdx.x, kvh = blockIdx.y, sl = blockIdx.z;
+  const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
+  const DecodeSeq sq = a.seqs[sl];
+  const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
+  const int n_isplits = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  if (split > n_isplits) return;
+
+  const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
+                      (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
+  __shared__ float pbuf_bf[G][64];
+  // P operand staging: hi rows (group, head) then lo rows; GQA <= 4: hi 0..7, lo 8..15,
+  // GQA 8: hi 0..15, lo 16..31
+  __shared__ _Float16 plds[32][64];
+  if (split == n_isplits) {
+    bf16_split<G>(a, sq, kvh, sl, split, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+    return;
+  }
+
+  // ---- prologue: query operands and per-head constants
+  v4i aop[HB][2];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      aop[hb][g] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + ((hb * 64 + lane) * 2 + g) * 16);
+  float cst[G][3];
+  const float* wc = reinterpret_cast<const float*>(ws + QP_CONST);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    cst[h][0] = wc[3 * h];
+    cst[h][1] = wc[3 * h + 1];
+    cst[h][2] = wc[3 * h + 2];
+  }
+  for (int i = lane; i < 32 * 64; i += 64) (&plds[0][0])[i] = static_cast<_Float16>(0.0f);
+  constexpr int LO_ROWS = (G == 8) ? 16 : 8;
+
+  // token of this lane after the Q.K row merge: tile order (0, 2, 1, 3) by 16-lane row
+  const int tile = ((q4 & 1) << 1) | (q4 >> 1);
+  const int tok = 16 * tile + n16;
+  const float pfac = __builtin_ldexpf(1.0f, 4 - vcode_exp(4 * (tok >> 5) + ((tok & 7) >> 1)));
+
+  float m_run[G], l_acc[G], lo_acc[2][G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m_run[h] = -INFINITY; l_acc[h] = 0.0f; lo_acc[0][h] = 0.0f; lo_acc[1][h] = 0.0f; }
+  // P.V accumulators: rows (grp, h) = grp * GP + h (16 rows cover GQA <= 8), columns = channels
+  v4f oacc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) oacc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int first = split * a.pages_per_split;
+  const int last = min(first + a.pages_per_split, n_pages);
+  const int32_t* ptab = a.page_table + static_cast<size_t>(sq.seq) * a.max_pages;
+  const size_t head_off = static_cast<size_t>(kvh) * HEAD_BLOCK;
+  const size_t page_stride = static_cast<size_t>(a.hkv) * HEAD_BLOCK;
+  __syncthreads();
+
+  for (int lp = first; lp < last; ++lp) {
+    const int page = ptab[lp];
+    const uint8_t* blk = a.pool + static_cast<size_t>(page) * page_stride + head_off;
+    const v4u* kp = reinterpret_cast<const v4u*>(blk + KC_OFF) + lane;
+    const v4u* vp = reinterpret_cast<const v4u*>(blk + VC_OFF) + lane;
+    const v4u kc0 = kp[0], kc1 = kp[64];
+    const v4u vc0 = vp[0], vc1 = vp[64];
+    const v4u md = *(reinterpret_cast<const v4u*>(blk + META_OFF) + tok);
+    const int n_valid = min(PAGE, sq.n_int2 - lp * PAGE);
+
+    // ---- Q.K on the matrix cores: acc[hb][t] rows (tau, grp, h4), columns = tokens of tile t
+    v4i acc[HB][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4u& kc = (t < 2) ? kc0 : kc1;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t w = kc[2 * (t & 1) + g];
+        const v4i b = {static_cast<int>(w & 0x03030303u), static_cast<int>((w >> 2) & 0x03030303u),
+                       static_cast<int>((w >> 4) & 0x03030303u), static_cast<int>((w >> 6) & 0x03030303u)};
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          if (g == 0) acc[hb][t] = v4i{0, 0, 0, 0};
+          acc[hb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[hb][g], b, acc[hb][t], 0, 0, 0);
+        }
+      }
+    }
+    // ---- merge rows across lanes: afterwards lane = token `tok`, x0/x1 = group 0/1 dot per head
+    float x0[GP], x1[GP];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto s01 = __builtin_amdgcn_permlane32_swap(acc[hb][0][r], acc[hb][1][r], false, false);
+        const auto s23 = __builtin_amdgcn_permlane32_swap(acc[hb][2][r], acc[hb][3][r], false, false);
+        const int c01 = static_cast<int>((static_cast<uint32_t>(s01[0]) << 7) + static_cast<uint32_t>(s01[1]));
+        const int c23 = static_cast<int>((static_cast<uint32_t>(s23[0]) << 7) + static_cast<uint32_t>(s23[1]));
+        const auto gg = __builtin_amdgcn_permlane16_swap(c01, c23, false, false);
+        x0[4 * hb + r] = static_cast<float>(static_cast<int>(gg[0]));
+        x1[4 * hb + r] = static_cast<float>(static_cast<int>(gg[1]));
+      }
+
+    // ---- scores (log2 units) and the running max
+    const float sk0 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.x & 0xFFFF)));
+    const float lk0 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.x >> 16)));
+    const float sk1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.y & 0xFFFF)));
+    const float lk1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.y >> 16)));
+    const bool valid = tok < n_valid;
+    float z[G];
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float y = fmaf(lk1, cst[h][2], fmaf(lk0, cst[h][1], fmaf(sk1, x1[h], sk0 * x0[h])));
+      const float sc = valid ? y * cst[h][0] : -INFINITY;
+      z[h] = sc - m_run[h];
+      zmax = fmaxf(zmax, z[h]);
+      x0[h] = sc;  // keep the score for the rescale path
+    }
+    if (__any(zmax > 0.0f)) {
+      // a new maximum: rescale everything accumulated so far (rare after the first pages)
+      float alpha[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m_run[h], lane_max(x0[h]));
+        alpha[h] = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
+        m_run[h] = mn;
+        z[h] = x0[h] - mn;
+        l_acc[h] *= alpha[h];
+        lo_acc[0][h] *= alpha[h];
+        lo_acc[1][h] *= alpha[h];
+      }
+      // oacc row 4 q4 + r: G <= 4 -> head r (lanes 0-31); G = 8 -> head 4 (q4 % 2) + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float al;
+        if (G == 8) al = (q4 & 1) ? alpha[(4 + r) % G] : alpha[r % G];
+        else al = (r < G) ? alpha[r % G] : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) oacc[ct][r] *= al;
+      }
+    }
+
+    // ---- probabilities, row sums, minimum terms, and the P operand staging
+    const float sv0 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.z & 0xFFFF)));
+    const float lv0 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.z >> 16)));
+    const float sv1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.w & 0xFFFF)));
+    const float lv1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.w >> 16)));
+    const float f0 = sv0 * pfac, f1 = sv1 * pfac;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = valid ? exp2f(z[h]) : 0.0f;
+      l_acc[h] += p;
+      lo_acc[0][h] = fmaf(p, lv0, lo_acc[0][h]);
+      lo_acc[1][h] = fmaf(p, lv1, lo_acc[1][h]);
+      const float a0 = p * f0, a1 = p * f1;
+      const _Float16 h0 = static_cast<_Float16>(a0), h1 = static_cast<_Float16>(a1);
+      plds[h][tok] = h0;
+      plds[GP + h][tok] = h1;
+      plds[LO_ROWS + h][tok] = static_cast<_Float16>(a0 - static_cast<float>(h0));
+      plds[LO_ROWS + GP + h][tok] = static_cast<_Float16>(a1 - static_cast<float>(h1));
+    }
+    __syncthreads();
+    // A operand rows (grp, h) = lane % 16: tokens 32 s + 8 (lane / 16) + 0..7
+    const v4u pa0 = *reinterpret_cast<const v4u*>(&plds[n16][8 * q4]);
+    const v4u pa1 = *reinterpret_cast<const v4u*>(&plds[n16][32 + 8 * q4]);
+    const v8h pA0 = __builtin_bit_cast(v8h, pa0), pA1 = __builtin_bit_cast(v8h, pa1);
+    v8h pB0 = pA0, pB1 = pA1;
+    if (G == 8) {
+      pB0 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(&plds[16 + n16][8 * q4]));
+      pB1 = __builtin_bit_cast(v8h, *reinterpret_cast<const v4u*>(&plds[16 + n16][32 + 8 * q4]));
+    }
+    __syncthreads();
+
+    // ---- P.V on the matrix cores, value codes as f16 denormals
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint32_t w = (ct < 4) ? vc0[ct & 3] : vc1[ct & 3];
+      const uint32_t lo4 = w << 4, hi6 = w >> 6;
+      const v8h b0 = as_h8(lo4 & 0x00300030u, lo4 & 0x00C000C0u, w & 0x00300030u, w & 0x00C000C0u);
+      const v8h b1 = as_h8(w & 0x03000300u, hi6 & 0x00300030u, hi6 & 0x00C000C0u, hi6 & 0x03000300u);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA0, b0, oacc[ct], 0, 0, 0);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA1, b1, oacc[ct], 0, 0, 0);
+      if (G == 8) {  // lo residual rows of the 16 (group, head) rows
+        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB0, b0, oacc[ct], 0, 0, 0);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB1, b1, oacc[ct], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: reduce per-lane sums, write (m, l, o) partials
+  float lsum[G], losum[2][G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lsum[h] = lane_sum(l_acc[h]);
+    losum[0][h] = lane_sum(lo_acc[0][h]);
+    losum[1][h] = lane_sum(lo_acc[1][h]);
+  }
+  const float two20 = 1048576.0f;
+  if (G <= 4) {
+    // rows 8..15 (lanes 32..63) hold the lo-residual products of rows 0..7: fold them in
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[ct][r] += __shfl_xor(oacc[ct][r], 32, 64);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* rec = a.part + ((static_cast<size_t>(sl) * a.hq + kvh * G + h) * a.n_split_max + split) * PART_STRIDE;
+    if (lane == 0) { rec[0] = m_run[h]; rec[1] = lsum[h]; }
+  }
+  // oacc[ct] row 4 q4 + r = grp * GP + h; channel 16 ct + n16 belongs to group ct / 4
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const int grp = ct >> 2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * q4 + r;
+      int h;
+      bool mine;
+      if (GP == 4) { h = row - 4 * grp; mine = (row >> 2) == grp && h < G; }
+      else { h = row - 8 * grp; mine = (row >> 3) == grp; }
+      if (mine) {
+        float* rec = a.part + ((static_cast<size_t>(sl) * a.hq + kvh * G + (h % G)) * a.n_split_max + split) * PART_STRIDE;
+        rec[2 + 16 * ct + n16] = fmaf(oacc[ct][r], two20, losum[grp][h % G]);
+      }
+    }
+  }
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+  const int gqa = a.hq / a.hkv;
+  const dim3 grid(a.n_split_max, a.hkv, a.n_seqs);
+  switch (gqa) {
+    case 1:
+      hipLaunchKernelGGL(k_qprep<1>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_decode_mfma<1>, grid, dim3(64), 0, s, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_qprep<2>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_decode_mfma<2>, grid, dim3(64), 0, s, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_qprep<4>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_decode_mfma<4>, grid, dim3(64), 0, s, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL(k_qprep<8>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_decode_mfma<8>, grid, dim3(64), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -77,6 +77,14 @@ hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s);
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// decode attention: prepared-query + split kernels (matrix-core path) or the reference-grade
+// fp32 kernel, then the split combine
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+
+// bytes of the prepared-query area that follows the split partials in the workspace,
+// per (sequence of a launch chunk, KV head)
+constexpr int QPREP_STRIDE = 8448;
 
 }  // namespace oscar

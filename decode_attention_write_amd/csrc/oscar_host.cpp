@@ -44,6 +44,7 @@ struct oscar_kv {
   std::vector<int32_t> table;  // host mirror [max_seqs][max_pages]
   std::deque<int32_t> fifo;
   int32_t pages_per_split = 0;
+  int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
   bool has_rotation = false;
 };
 
@@ -368,7 +369,8 @@ int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int
   for (int i = 0; i < n_seqs; ++i)
     max_split = std::max(max_split, ceil_div(ceil_div(kv->n_int2[seq_ids[i]], kPage), pps) + 1);
   const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
-  *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float);
+  *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float) +
+           static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE;
   return OSCAR_OK;
 }
 
@@ -414,7 +416,8 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     }
     a.n_split_max = static_cast<int32_t>(max_split);
     a.scale_log2 = sm_scale * 1.4426950408889634f;
-    hipError_t e = launch_decode(a, st);
+    hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st) : launch_decode_mfma(a, st);
+    if (e == hipSuccess) e = launch_combine(a, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_decode_attn: launch");
   }
   return OSCAR_OK;
@@ -454,6 +457,12 @@ int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, void* stream) {
   kv->len[seq] = 0;
   kv->n_int2[seq] = 0;
   return push_table(kv, upd, as_stream(stream));
+}
+
+int oscar_kv_set_decode_kernel(oscar_kv* kv, int32_t kernel) {
+  if (!kv || kernel < 0 || kernel > 1) { set_error("oscar_kv_set_decode_kernel: kernel must be 0 or 1"); return OSCAR_E_ARG; }
+  kv->decode_kernel = kernel;
+  return OSCAR_OK;
 }
 
 int oscar_kv_set_decode_split(oscar_kv* kv, int32_t pages_per_split) {

@@ -237,6 +237,11 @@ int oscar_kv_reset_seq(oscar_kv *kv, int32_t seq, void *stream);
 /* Decode tuning: pages_per_split = 0 picks a split size from the batch. */
 int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);
 
+/* Decode kernel: 0 (default) = the matrix-core kernel (i8 MFMA for q.k on the raw
+ * codes, f16 MFMA for p.v); 1 = the reference-grade kernel that dequantizes every
+ * element in fp32 (slow; kept as an independent cross-check). */
+int oscar_kv_set_decode_kernel(oscar_kv *kv, int32_t kernel);
+
 const char *oscar_last_error(void);
 void oscar_kv_destroy(oscar_kv *kv);
 

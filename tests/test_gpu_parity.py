@@ -231,16 +231,24 @@ def test_evict_append_decode_cycle(gpu_lib):
         assert st.seq_info(s) == (470, 470 - 320)
 
 
-def test_split_count_invariance_determinism_page_order(gpu_lib):
+@pytest.mark.parametrize("kernel", [0, 1])
+def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
+    """Outputs do not depend on the split size (beyond rounding), repeat bitwise, and do not depend
+    on where the pages sit in the pool.  The fp32 reference kernel (1) agrees across splits to 1e-6;
+    the matrix-core kernel (0) rounds p*s to an fp16 pair relative to each split's running maximum,
+    so its split decompositions agree to 1e-4 (an order below the 1e-3 parity bound)."""
     hkv, hq, L = 2, 8, 320 + 64 * 37 + 5
-    _case("split invariance / determinism / page order")
+    _case(f"split invariance / determinism / page order, kernel {kernel}")
     rot = parity.calibrate(synth.CFG_QWEN3_4B, 3, hkv)
     ks, vs = _kv_batch(synth.CFG_QWEN3_4B, [0, 1], hkv, L)
-    q = parity.to_dev_bf16(synth.decode_queries(synth.CFG_QWEN3_4B, 3, 2, hq, hkv))
+    qb = synth.decode_queries(synth.CFG_QWEN3_4B, 3, 2, hq, hkv)
+    q = parity.to_dev_bf16(qb)
     outs = {}
+    gpu = None
     for order in ("identity", "shuffled"):
         free = np.arange(80) if order == "identity" else synth.page_permutation(synth.CFG_QWEN3_4B, 3, 80)
         st = _store(gpu_lib, hq, hkv, 2, 40, 80, free, rot)
+        st.set_decode_kernel(kernel)
         st.write([0, 1], parity.to_dev_bf16(ks), parity.to_dev_bf16(vs))
         for pps in (1, 3, 38, 0):
             st.set_decode_split(pps)
@@ -248,11 +256,17 @@ def test_split_count_invariance_determinism_page_order(gpu_lib):
             b = st.decode([0, 1], q, SCALE).cpu().numpy()
             assert np.array_equal(a, b), "decode is not deterministic"
             outs[(order, pps)] = a
+        gpu = parity.export(st)
+        lens = np.array([L, L])
+        iso = attention.decode(gpu[0], gpu[1], gpu[2], lens, lens - 320, rot, qb, [0, 1], SCALE, hq)
+        err = parity.rel_l2(outs[(order, 0)], iso)
+        print(f"[parity] kernel {kernel} {order}: rel-l2 vs oracle {err:.2e}", flush=True)
+        assert err <= ISO_TOL
     base = outs[("identity", 0)]
+    tol = 1e-6 if kernel == 1 else 1e-4
     for key, o in outs.items():
-        assert parity.rel_l2(o, base) <= 1e-6, key
-        if key[1] == 0 or key[1] == 3:
-            assert np.array_equal(o, outs[("identity", key[1])]), key
+        assert parity.rel_l2(o, base) <= tol, key
+        assert np.array_equal(o, outs[("identity", key[1])]), key   # page order invariance
 
 
 def test_qwen3_4b_shape_small_context(gpu_lib):
