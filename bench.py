@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--attn-reps", type=int, default=3)
     ap.add_argument("--cpu-units", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
+    ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
+    ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -149,6 +152,8 @@ def main():
     for l in range(n_layers):
         st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, l, num_pages))
         st.set_rotation(rots[l])
+        st.set_decode_split(args.pps)
+        st.set_decode_kernel(args.kernel)
         prm = sgpu.HeadParams(cfg, l, hkv)
         for s in range(B):
             sgpu.draw_kv(prm, s, 0, ctx, kbuf[0], vbuf[0])
@@ -218,6 +223,27 @@ def main():
     ms_per_step = gpu_ms / args.steps
     step_gbps = sum(bytes_per_step) / (gpu_ms / 1e3) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms/step), {step_gbps:.0f} GB/s")
+
+    # ---- development sweep of the split size (attention only)
+    for pps in [int(x) for x in args.sweep_pps.split(",") if x]:
+        for st in stores:
+            st.set_decode_split(pps)
+        need = max(st.workspace_bytes(seqs) for st in stores)
+        if need > ws.numel() * 4:
+            ws = torch.empty(need // 4 + 1, dtype=torch.float32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for st in stores:
+            st.decode(seqs, qs[0], scale, out=outs[0], ws=ws)
+        e0.record()
+        for r in range(2):
+            for l, st in enumerate(stores):
+                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (2 * n_layers)
+        log(f"sweep pps={pps}: {us:.1f} us/layer, {2.085e9 / us / 1e3:.0f} GB/s")
+    for st in stores:
+        st.set_decode_split(args.pps)
 
     # ---- attention-only pass over the frozen cache: per-call HIP events on the launch stream
     per_call = []

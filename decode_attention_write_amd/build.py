@@ -28,7 +28,8 @@ SOURCES = {
     "calibrate.cpp": [],
     "write.hip": ["-ffp-contract=off"],
     "decode.hip": [],
-    "decode_mfma.hip": [],
+    # keep MFMA accumulators in arch VGPRs (no AGPR copies around the running rescale)
+    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -138,7 +138,7 @@ __device__ inline int vcode_exp(int p) {
 // ------------------------------------------------------------------ BF16 sink + window split
 // One wavefront: lane = ring slot for the scores, lane = channel pair for the value product.
 template <int G>
-__device__ void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, const float* qf,
+__device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, const float* qf,
                            float (*pbuf)[64]) {
   const int lane = threadIdx.x;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
@@ -239,14 +239,14 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
       aop[hb][g] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + ((hb * 64 + lane) * 2 + g) * 16);
+  // per-head constants are wave-uniform: keep them in scalar registers
   float cst[G][3];
   const float* wc = reinterpret_cast<const float*>(ws + QP_CONST);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    cst[h][0] = wc[3 * h];
-    cst[h][1] = wc[3 * h + 1];
-    cst[h][2] = wc[3 * h + 2];
-  }
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+      cst[h][k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wc[3 * h + k])));
   for (int i = lane; i < 32 * 64; i += 64) (&plds[0][0])[i] = static_cast<_Float16>(0.0f);
   constexpr int LO_ROWS = (G == 8) ? 16 : 8;
 
@@ -270,14 +270,35 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
   const size_t page_stride = static_cast<size_t>(a.hkv) * HEAD_BLOCK;
   __syncthreads();
 
-  for (int lp = first; lp < last; ++lp) {
-    const int page = ptab[lp];
+  // Raw page block (128-bit loads): key codes (2 per lane), value codes (2 per lane), and the
+  // metadata of this lane's token.  Pages are loaded one ahead into two register sets that
+  // alternate, always issuing the next load (clamped to the last page) so the wait counts stay
+  // exact.  Page ids come from a 64-entry vector of the page-table row via readlane.
+  struct Raw { v4u kc0, kc1, vc0, vc1, md; };
+  int pbase = first;
+  int pvec = ptab[min(first + lane, max(first, last - 1))];
+  auto load_page = [&](int lpn, Raw& r) {
+    if (lpn - pbase >= 64) {
+      pbase += 64;
+      pvec = ptab[min(pbase + lane, last - 1)];
+    }
+    const int page = __builtin_amdgcn_readlane(pvec, lpn - pbase);
     const uint8_t* blk = a.pool + static_cast<size_t>(page) * page_stride + head_off;
     const v4u* kp = reinterpret_cast<const v4u*>(blk + KC_OFF) + lane;
     const v4u* vp = reinterpret_cast<const v4u*>(blk + VC_OFF) + lane;
-    const v4u kc0 = kp[0], kc1 = kp[64];
-    const v4u vc0 = vp[0], vc1 = vp[64];
-    const v4u md = *(reinterpret_cast<const v4u*>(blk + META_OFF) + tok);
+    r.kc0 = __builtin_nontemporal_load(kp);
+    r.kc1 = __builtin_nontemporal_load(kp + 64);
+    r.vc0 = __builtin_nontemporal_load(vp);
+    r.vc1 = __builtin_nontemporal_load(vp + 64);
+    r.md = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(blk + META_OFF) + tok);
+  };
+
+  auto process_page = [&](int lp, const Raw& raw) {
+    const v4u& kc0 = raw.kc0;
+    const v4u& kc1 = raw.kc1;
+    const v4u& vc0 = raw.vc0;
+    const v4u& vc1 = raw.vc1;
+    const v4u& md = raw.md;
     const int n_valid = min(PAGE, sq.n_int2 - lp * PAGE);
 
     // ---- Q.K on the matrix cores: acc[hb][t] rows (tau, grp, h4), columns = tokens of tile t
@@ -333,8 +354,9 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
       float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m_run[h], lane_max(x0[h]));
-        alpha[h] = (m_run[h] == -INFINITY) ? 0.0f : exp2f(m_run[h] - mn);
+        const float mn = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+            __builtin_bit_cast(int, fmaxf(m_run[h], lane_max(x0[h])))));
+        alpha[h] = (m_run[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
         m_run[h] = mn;
         z[h] = x0[h] - mn;
         l_acc[h] *= alpha[h];
@@ -360,7 +382,8 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
     const float f0 = sv0 * pfac, f1 = sv1 * pfac;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float p = valid ? exp2f(z[h]) : 0.0f;
+      // z <= 0 here; the raw exp2 flushes results below 2^-126 to zero, which is harmless
+      const float p = valid ? __builtin_amdgcn_exp2f(z[h]) : 0.0f;
       l_acc[h] += p;
       lo_acc[0][h] = fmaf(p, lv0, lo_acc[0][h]);
       lo_acc[1][h] = fmaf(p, lv1, lo_acc[1][h]);
@@ -396,6 +419,18 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
         oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB0, b0, oacc[ct], 0, 0, 0);
         oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB1, b1, oacc[ct], 0, 0, 0);
       }
+    }
+  };
+
+  if (first < last) {
+    Raw bx, by;
+    load_page(first, bx);
+    for (int lp = first; lp < last; lp += 2) {
+      load_page(min(lp + 1, last - 1), by);
+      process_page(lp, bx);
+      if (lp + 1 >= last) break;
+      load_page(min(lp + 2, last - 1), bx);
+      process_page(lp + 1, by);
     }
   }
 
@@ -437,6 +472,37 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
       }
     }
   }
+}
+
+template <typename K>
+static int resident_for(K kernel, int block) {
+  int dev = 0, n_cu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+  return n_cu * per_cu;
+}
+
+int decode_resident_workgroups(int gqa, int kernel) {
+  static int cache[2][9] = {};
+  const int k = kernel ? 1 : 0;
+  if (gqa < 1 || gqa > 8) return 1024;
+  if (cache[k][gqa] == 0) {
+    int r = 0;
+    if (k == 1) {
+      r = 1024;  // reference kernel: 256 threads per work-group
+    } else {
+      switch (gqa) {
+        case 1: r = resident_for(k_decode_mfma<1>, 64); break;
+        case 2: r = resident_for(k_decode_mfma<2>, 64); break;
+        case 4: r = resident_for(k_decode_mfma<4>, 64); break;
+        case 8: r = resident_for(k_decode_mfma<8>, 64); break;
+        default: r = 0;
+      }
+    }
+    cache[k][gqa] = r > 0 ? r : 1024;
+  }
+  return cache[k][gqa];
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {

@@ -82,6 +82,8 @@ hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+// work-groups of the decode split kernel resident on the current device at once
+int decode_resident_workgroups(int gqa, int kernel);
 
 // bytes of the prepared-query area that follows the split partials in the workspace,
 // per (sequence of a launch chunk, KV head)

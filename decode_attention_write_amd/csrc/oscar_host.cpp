@@ -113,18 +113,34 @@ int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd
 
 int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
   if (kv->pages_per_split > 0) return kv->pages_per_split;
-  int64_t total = 0, max_pages = 0;
-  for (int i = 0; i < n_seqs; ++i) {
-    const int64_t p = ceil_div(kv->n_int2[seq_ids[i]], kPage);
-    total += p;
-    max_pages = std::max(max_pages, p);
+  // Work-groups of the split kernel that fit on the device at once (the matrix-core kernel uses
+  // one wavefront per work-group).  Aim for a single residency round holding as many waves as
+  // fit: INT2 splits + one sink/window split per (sequence, KV head) <= resident capacity, for
+  // each launch chunk of up to CHUNK sequences.
+  if (kv->plan_only) return 64;
+  const int64_t resident = decode_resident_workgroups(kv->desc.num_q_heads / kv->desc.num_kv_heads,
+                                                      kv->decode_kernel);
+  const int64_t hkv = kv->desc.num_kv_heads;
+  int64_t best = 1;
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    const int n = std::min(CHUNK, n_seqs - c0);
+    int64_t max_pages = 0, total = 0;
+    for (int i = c0; i < c0 + n; ++i) {
+      const int64_t p = ceil_div(kv->n_int2[seq_ids[i]], kPage);
+      max_pages = std::max(max_pages, p);
+      total += p;
+    }
+    if (max_pages == 0) continue;
+    const int64_t budget = std::max<int64_t>(n * hkv, resident - n * hkv);
+    int64_t pps = std::max<int64_t>(1, ceil_div(total * hkv, budget));
+    for (; pps < max_pages; ++pps) {
+      int64_t wgs = 0;
+      for (int i = c0; i < c0 + n; ++i) wgs += ceil_div(ceil_div(kv->n_int2[seq_ids[i]], kPage), pps);
+      if (wgs * hkv <= budget) break;
+    }
+    best = std::max(best, pps);
   }
-  // aim at ~4 work-groups per compute unit over the whole call (256 CUs)
-  const int64_t target_wg = 1024;
-  const int64_t units = total * kv->desc.num_kv_heads;
-  int64_t pps = std::max<int64_t>(8, ceil_div(units, target_wg));
-  pps = std::min<int64_t>(pps, std::max<int64_t>(1, max_pages));
-  return std::max<int64_t>(1, pps);
+  return best;
 }
 
 }  // namespace

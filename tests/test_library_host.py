@@ -126,9 +126,10 @@ def test_workspace_bytes_and_split_choice():
     s = _plan_store(max_pages=64, num_pages=64)
     s.write([0], None, None, n_new=320 + 64 * 20)
     s.write([1], None, None, n_new=100)
+    qprep = 2 * 2 * 8448          # prepared-query area: 2 seqs x 2 KV heads
     nb = s.workspace_bytes([0, 1])
-    assert nb > 0 and nb % (130 * 4) == 0
+    assert nb > qprep and (nb - qprep) % (130 * 4) == 0
     s.set_decode_split(4)
     nb4 = s.workspace_bytes([0, 1])
-    # 20 pages / 4 per split = 5 INT2 splits + 1 BF16 split, 2 seqs x 8 q heads
-    assert nb4 == 2 * 8 * 6 * 130 * 4
+    # 20 pages / 4 per split = 5 INT2 splits + 1 BF16 split, 2 seqs x 8 q heads, 130 floats each
+    assert nb4 == 2 * 8 * 6 * 130 * 4 + qprep
