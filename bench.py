@@ -30,14 +30,49 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_bytes(lens, n2s, hq, hkv):
-    """Algorithmic bytes of one decode_attn call (per layer)."""
+def split_kernel_bytes(lens, n2s, hkv):
+    """Algorithmic bytes of one launch of the decode split kernel: per (sequence, KV head) the
+    INT2 tokens (32 B key codes + 32 B value codes + 16 B scales/minimums) and the BF16 sink and
+    window tokens (256 B key + 256 B value row), plus each sequence's page ids."""
     b = 0
     for L, n2 in zip(lens, n2s):
-        b += hkv * (80 * n2 + 512 * min(L, 320))
-        b += hq * 128 * (2 + 4)
+        b += hkv * (80 * n2 + 512 * (L - n2))
         b += 4 * (-(-n2 // 64))
-    return b + hkv * 128 * 128 * 4
+    return b
+
+
+def decode_bytes(lens, n2s, hq, hkv):
+    """Algorithmic bytes of one decode_attn call (per layer): the split kernel's, the bf16
+    queries read, the fp32 outputs written and the fp32 rotations read once."""
+    return split_kernel_bytes(lens, n2s, hkv) + len(lens) * hq * 128 * (2 + 4) + hkv * 128 * 128 * 4
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "k_decode_mfma_g4_100k_b32_traffic.txt")
+KERNEL_SOURCES = ["decode_mfma.hip", "common.h", "launch.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_write_amd", "csrc",
+                               name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per split-kernel launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken (or no summary exists)."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(kv["hbm_bytes_per_launch"])
 
 
 def evict_bytes(n_seqs, hkv):
@@ -48,34 +83,52 @@ def append_bytes(n_seqs, hkv):
     return n_seqs * hkv * (512 + 512) + hkv * 128 * 128 * 4
 
 
-def cpu_baseline(rots, lens0, q_layer0, out_layer0, hq, hkv, cfg, context, n_units, total_units, step_bytes_attn):
-    """Time the oracle's decode attention on sampled (layer 0, seq, kv head) units, one core."""
+CPU_UNITS = [(0, 0), (17, 5), (31, 3), (9, 7)]
+
+
+def export_units(st, seqs_kv):
+    """Host copies of the store state of (seq, kv head) units: their pages, ring slots, lengths."""
+    import numpy as np
+    import torch
+    torch.cuda.synchronize()
+    table = st.page_table()
+    out = []
+    for s, kv in seqs_kv:
+        L, n2 = st.seq_info(s)
+        n_pages = -(-n2 // 64)
+        pages = torch.from_numpy(table[s, :n_pages].astype(np.int64)).cuda()
+        pool_u = st.pool_view()[pages, kv].cpu().numpy()[:, None, :]          # [n_pages, 1, 5120]
+        ring_u = st.ring_view()[s, kv].cpu().numpy().view(np.uint16)[None, None]  # [1, 1, 2, 320, 128]
+        out.append((s, kv, L, n2, pool_u, ring_u))
+    return out
+
+
+def cpu_baseline(units, rots, q_layer0, out_layer0, hq, hkv, total_units, step_bytes_attn):
+    """Time the oracle's decode attention on sampled (layer 0, seq, kv head) units, one core.
+
+    The oracle runs on the GPU's exported store state of each unit (identical inputs), so the
+    reported rel-L2 is the decode parity figure; its time is extrapolated to the whole step.
+    """
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    import synth
-    from oracle import attention, store as ostore
+    from oracle import attention
     g = hq // hkv
-    units = [(s, kv) for s, kv in [(0, 0), (17, 5), (31, 3), (9, 7)]][:n_units]
-    t_build = t_dec = 0.0
+    t_dec = 0.0
     errs = []
-    for s, kv in units:
-        t0 = time.perf_counter()
-        kb, vb = synth.unit_kv(cfg, 0, s, kv, context)
-        st = ostore.OracleStore(1, 1, -(-context // 64), -(-context // 64), range(-(-context // 64)), rots[0][kv:kv + 1])
-        st.write([0], kb[None, :, None, :], vb[None, :, None, :])
+    for s, kv, L, n2, pool_u, ring_u in units:
+        table_u = np.arange(pool_u.shape[0], dtype=np.int32)[None, :]
         t1 = time.perf_counter()
-        out = attention.decode_store(st, q_layer0[s:s + 1, kv * g:(kv + 1) * g], [0], 1 / math.sqrt(128), g)
+        out = attention.decode(pool_u, ring_u, table_u, np.array([L]), np.array([n2]), rots[0][kv:kv + 1],
+                               q_layer0[s:s + 1, kv * g:(kv + 1) * g], [0], 1 / math.sqrt(128), g)
         t2 = time.perf_counter()
-        t_build += t1 - t0
         t_dec += t2 - t1
-        ref = out[0]
         gpu = out_layer0[s, kv * g:(kv + 1) * g]
-        errs.append(float(np.linalg.norm(gpu - ref) / np.linalg.norm(ref)))
-        log(f"cpu oracle unit seq={s} kv={kv}: build {t1 - t0:.1f}s decode {t2 - t1:.2f}s rel-l2 vs gpu {errs[-1]:.2e}")
+        errs.append(float(np.linalg.norm(gpu - out[0]) / np.linalg.norm(out[0])))
+        log(f"cpu oracle unit seq={s} kv={kv} ({L} tokens): decode {t2 - t1:.2f}s, rel-l2 vs gpu {errs[-1]:.2e}")
     if limiter is not None:
         limiter.unregister()
     per_unit = t_dec / len(units)
@@ -85,9 +138,9 @@ def cpu_baseline(rots, lens0, q_layer0, out_layer0, hq, hkv, cfg, context, n_uni
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{len(units)} of {total_units} (layer, seq, kv-head) units of the attention pass, "
-                   f"{context}-token context each, decode attention only (state building "
-                   f"{t_build / len(units):.1f}s/unit untimed), extrapolated x{total_units}"),
+        "sample": (f"{len(units)} of {total_units} (layer, seq, kv-head) units of the attention pass "
+                   f"(oracle on the GPU's exported store of each unit, 100000-token context), decode "
+                   f"attention only, extrapolated x{total_units}"),
         "seconds_per_unit": per_unit,
         "sample_rel_l2_vs_gpu": max(errs),
     }
@@ -102,7 +155,9 @@ def main():
     ap.add_argument("--context", type=int, default=100000, help="development only")
     ap.add_argument("--batch", type=int, default=32, help="development only")
     ap.add_argument("--attn-reps", type=int, default=3)
-    ap.add_argument("--cpu-units", type=int, default=2)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="run a plain device copy of this size at the end (counter scaling in profiled runs)")
+    ap.add_argument("--cpu-units", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
     ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
@@ -186,7 +241,7 @@ def main():
     torch.cuda.synchronize()
     out_layer0 = outs[0].cpu().numpy()
     q_layer0 = qs[0].cpu().numpy().view(np.uint16)
-    lens0 = [stores[0].seq_info(s) for s in seqs]
+    units0 = [] if args.no_cpu_baseline else export_units(stores[0], CPU_UNITS[:args.cpu_units])
 
     def step(i):
         for l in range(n_layers):
@@ -251,6 +306,12 @@ def main():
     for st in stores:
         info = [st.seq_info(s) for s in seqs]
         attn_bytes.append(decode_bytes([L for L, _ in info], [n2 for _, n2 in info], hq, hkv))
+    kbytes = []
+    for st in stores:
+        info = [st.seq_info(s) for s in seqs]
+        kbytes.append(split_kernel_bytes([L for L, _ in info], [n2 for _, n2 in info], hkv))
+    for st in stores:
+        st.set_decode_timing(True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
     for r in range(args.attn_reps):
         for l, st in enumerate(stores):
@@ -259,6 +320,18 @@ def main():
             evs[l][1].record()
         torch.cuda.synchronize()
         per_call.extend(a.elapsed_time(b) for a, b in evs)
+    k_launches, k_ms = 0, 0.0
+    for st in stores:
+        n, ms = st.read_decode_timing()
+        k_launches += n
+        k_ms += ms
+        st.set_decode_timing(False)
+    n_chunks = -(-B // 64)
+    assert k_launches == args.attn_reps * n_layers * n_chunks, k_launches
+    kernel_us = k_ms * 1e3 / k_launches
+    kernel_bytes = float(np.mean(kbytes)) / n_chunks
+    kernel_gbps = kernel_bytes / (kernel_us / 1e6) / 1e9
+    log(f"split kernel: {kernel_us:.1f} us/launch, {kernel_gbps:.0f} GB/s ({100 * kernel_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
     attn_ms = float(np.mean(per_call))
     attn_gbps = float(np.mean(attn_bytes)) / (attn_ms / 1e3) / 1e9
     log(f"attention-only: {attn_ms * 1e3:.1f} us/layer, {attn_gbps:.0f} GB/s ({100 * attn_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
@@ -290,19 +363,30 @@ def main():
                       "bytes_per_layer": int(np.mean(attn_bytes))},
         "roofline": {
             "bound": "hbm",
-            "achieved": round(attn_gbps, 1),
+            "achieved": round(kernel_gbps, 1),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(attn_gbps / PEAK_GBPS, 4),
-            "traffic": None,
-            "kernel": "decode attention call (split-K kernel + combine), per layer",
+            "frac": round(kernel_gbps / PEAK_GBPS, 4),
+            "traffic": measured_traffic() if full else None,
+            "kernel": f"k_decode_mfma<{hq // hkv}> (split-K decode attention over the INT2 pages and BF16 ring)",
+            "us_per_launch": round(kernel_us, 2),
+            "bytes_per_launch": int(kernel_bytes),
         },
     }
+    if args.copy_calib_mib:
+        # a plain copy of known size, for scaling the memory counters of a profiled run
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
     if not args.no_cpu_baseline:
         total_units = n_layers * B * hkv
         step_attn_bytes = float(np.sum(attn_bytes))
-        result["cpu_baseline"] = cpu_baseline(rots, lens0, q_layer0, out_layer0, hq, hkv, cfg, ctx,
-                                              args.cpu_units, total_units, step_attn_bytes)
+        result["cpu_baseline"] = cpu_baseline(units0, rots, q_layer0, out_layer0, hq, hkv, total_units,
+                                              step_attn_bytes)
     print(json.dumps(result), flush=True)
 
 

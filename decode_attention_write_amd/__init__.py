@@ -36,7 +36,8 @@ EXPORTS = [
     "oscar_calibrate_host", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
-    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_last_error", "oscar_kv_destroy",
+    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_decode_timing",
+    "oscar_kv_read_decode_timing", "oscar_last_error", "oscar_kv_destroy",
 ]
 
 
@@ -81,6 +82,8 @@ def load():
         "oscar_kv_reset_seq": [P, I32, P],
         "oscar_kv_set_decode_split": [P, I32],
         "oscar_kv_set_decode_kernel": [P, I32],
+        "oscar_kv_set_decode_timing": [P, I32],
+        "oscar_kv_read_decode_timing": [P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -254,6 +257,17 @@ class KVStore:
     def set_decode_kernel(self, kernel):
         """0 = matrix-core kernel (default), 1 = reference-grade fp32 kernel."""
         _check(load().oscar_kv_set_decode_kernel(self.handle, int(kernel)))
+
+    def set_decode_timing(self, enable=True):
+        """Record HIP events around every launch of the decode split kernel (measurement aid)."""
+        _check(load().oscar_kv_set_decode_timing(self.handle, int(bool(enable))))
+
+    def read_decode_timing(self):
+        """(timed launches, summed split-kernel milliseconds) since the last read; waits for them."""
+        n = ctypes.c_int32(0)
+        ms = ctypes.c_double(0.0)
+        _check(load().oscar_kv_read_decode_timing(self.handle, ctypes.byref(n), ctypes.byref(ms)))
+        return n.value, ms.value
 
     # ---- views of the device buffers (for tests and export)
     def pool_view(self):

@@ -190,15 +190,34 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a) {
   const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
   const int n_split = (n_pages + a.pages_per_split - 1) / a.pages_per_split + 1;
   const float* rec0 = a.part + (static_cast<size_t>(sl) * a.hq + h) * a.n_split_max * PART_STRIDE;
+  __shared__ float wsh[128];
+  __shared__ float red[2];
+  // split weights 2^(m_i - M), loaded in parallel (one split per thread, 128 at a time)
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, rec0[s * PART_STRIDE]);
+  for (int s0 = c; s0 < n_split; s0 += 128) M = fmaxf(M, rec0[static_cast<size_t>(s0) * PART_STRIDE]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if ((c & 63) == 0) red[c >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
   float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < n_split; ++s) {
-    const float m = rec0[s * PART_STRIDE];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L = fmaf(w, rec0[s * PART_STRIDE + 1], L);
-    O = fmaf(w, rec0[s * PART_STRIDE + 2 + c], O);
+  for (int b = 0; b < n_split; b += 128) {
+    __syncthreads();
+    const int s = b + c;
+    float w = 0.0f;
+    if (s < n_split) {
+      const float m = rec0[static_cast<size_t>(s) * PART_STRIDE];
+      w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    }
+    wsh[c] = w;
+    __syncthreads();
+    const int nb = min(128, n_split - b);
+#pragma unroll 4
+    for (int i = 0; i < nb; ++i) {
+      const float* rec = rec0 + static_cast<size_t>(b + i) * PART_STRIDE;
+      L = fmaf(wsh[i], rec[1], L);
+      O = fmaf(wsh[i], rec[2 + c], O);
+    }
   }
   a.out[(static_cast<size_t>(sq.src) * a.hq + h) * D + c] = O / L;
 }
@@ -208,15 +227,23 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const dim3 grid(a.n_split_max, a.hkv, a.n_seqs);
   const int gqa = a.hq / a.hkv;
+  if (t0) {
+    const hipError_t e = hipEventRecord(t0, s);
+    if (e != hipSuccess) return e;
+  }
   switch (gqa) {
     case 1: hipLaunchKernelGGL(k_decode_simple<1>, grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_decode_simple<2>, grid, dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL(k_decode_simple<4>, grid, dim3(256), 0, s, a); break;
     case 8: hipLaunchKernelGGL(k_decode_simple<8>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
+  }
+  if (t1) {
+    const hipError_t e = hipEventRecord(t1, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -59,11 +59,17 @@ __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
   const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
   const uint16_t* q = a.q + (static_cast<size_t>(sq.src) * a.hq + static_cast<size_t>(kvh) * G) * D;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.part) + qprep_offset(a) + (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
+  __shared__ float qin[G][D];
+  for (int idx = tid; idx < G * D; idx += 256) qin[idx / D][idx % D] = bf16_to_f32(q[idx]);
+  __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, c = idx % D;
-    float acc = 0.0f;
-    for (int i = 0; i < D; ++i) acc = fmaf(bf16_to_f32(q[h * D + i]), rot[i * D + c], acc);
-    qf[h][c] = acc * a.scale_log2;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int i = 0; i < D; i += 4)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = fmaf(qin[h][i + u], rot[(i + u) * D + c], acc[u]);
+    qf[h][c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale_log2;
   }
   __syncthreads();
   for (int h = tid >> 6; h < G; h += 4) {
@@ -136,35 +142,49 @@ __device__ inline int vcode_exp(int p) {
 }
 
 // ------------------------------------------------------------------ BF16 sink + window split
-// One wavefront: lane = ring slot for the scores, lane = channel pair for the value product.
+// One wavefront over the ring in five 64-slot chunks.  Scores: lane = ring slot, the lane reads
+// its own key row (all sixteen 16-byte pieces in flight at once).  Value product: lane = channel
+// pair, token rows read in batches of 16 so that 16 loads are in flight.  Slots that hold no
+// token are masked by a wave-uniform ballot; their (possibly uninitialised) rows never reach
+// the sums.
 template <int G>
 __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, const float* qf,
                            float (*pbuf)[64]) {
+  constexpr int KB = (G == 8) ? 4 : 8;    // key pieces in flight per lane
+  constexpr int VB = 8;                  // value rows in flight
   const int lane = threadIdx.x;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
+  const uint16_t* kring = a.ring + ring_head;
+  const uint16_t* vring = kring + static_cast<size_t>(RING) * D;
   const int n_win = max(0, sq.len - SINK - sq.n_int2);
+  const int n_sink = min(sq.len, SINK);
+  const int wfirst = sq.n_int2 % WIN;     // window position of the oldest window token
   float m[G], l[G], o0[G], o1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.0f; o0[h] = 0.0f; o1[h] = 0.0f; }
   for (int ch = 0; ch < RING / 64; ++ch) {
     const int slot = ch * 64 + lane;
-    const bool ok = (slot < SINK) ? (slot < min(sq.len, SINK))
-                                  : (((slot - SINK - (sq.n_int2 % WIN) + WIN) % WIN) < n_win);
-    if (!__any(ok)) continue;
+    const bool ok = (slot < SINK) ? (slot < n_sink) : (((slot - SINK - wfirst + WIN) % WIN) < n_win);
+    const uint64_t okmask = __ballot(ok);
+    if (okmask == 0) continue;
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.0f;
-    if (ok) {
-      const uint4* kr = reinterpret_cast<const uint4*>(a.ring + ring_head + static_cast<size_t>(slot) * D);
-#pragma unroll 4
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        const uint4 w = kr[c8];
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const uint4* kr = reinterpret_cast<const uint4*>(kring + static_cast<size_t>(slot) * D);
+#pragma unroll 1
+    for (int c0 = 0; c0 < D / 8; c0 += KB) {
+      uint4 w[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) w[i] = kr[c0 + i];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float k0 = __uint_as_float(ww[e] << 16), k1 = __uint_as_float(ww[e] & 0xFFFF0000u);
+          const int c = 8 * (c0 + i) + 2 * e;
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[h] = fmaf(qf[h * D + 8 * c8 + 2 * e + 1], k1, fmaf(qf[h * D + 8 * c8 + 2 * e], k0, s[h]));
+          for (int h = 0; h < G; ++h) s[h] = fmaf(qf[h * D + c + 1], k1, fmaf(qf[h * D + c], k0, s[h]));
         }
       }
     }
@@ -182,17 +202,23 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
     }
     __syncthreads();
     // value product: lane owns channels 2 lane, 2 lane + 1
-    for (int j = 0; j < 64; ++j) {
-      const int sj = ch * 64 + j;
-      const bool okj = (sj < SINK) ? (sj < min(sq.len, SINK))
-                                   : (((sj - SINK - (sq.n_int2 % WIN) + WIN) % WIN) < n_win);
-      if (!okj) continue;  // uniform across the wave
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(a.ring + ring_head + static_cast<size_t>(RING + sj) * D + 2 * lane);
-      const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xFFFF0000u);
+    const uint32_t* vr = reinterpret_cast<const uint32_t*>(vring + static_cast<size_t>(ch * 64) * D) + lane;
+#pragma unroll 1
+    for (int j0 = 0; j0 < 64; j0 += VB) {
+      if (((okmask >> j0) & ((1ull << VB) - 1)) == 0) continue;  // wave-uniform
+      uint32_t w[VB];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        o0[h] = fmaf(pbuf[h][j], v0, o0[h]);
-        o1[h] = fmaf(pbuf[h][j], v1, o1[h]);
+      for (int j = 0; j < VB; ++j) w[j] = vr[(j0 + j) * (D / 2)];
+#pragma unroll
+      for (int j = 0; j < VB; ++j) {
+        const bool okj = (okmask >> (j0 + j)) & 1;
+        const float v0 = okj ? __uint_as_float(w[j] << 16) : 0.0f;
+        const float v1 = okj ? __uint_as_float(w[j] & 0xFFFF0000u) : 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          o0[h] = fmaf(pbuf[h][j0 + j], v0, o0[h]);
+          o1[h] = fmaf(pbuf[h][j0 + j], v1, o1[h]);
+        }
       }
     }
     __syncthreads();
@@ -208,7 +234,7 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
 
 // ------------------------------------------------------------------ INT2 page loop
 // Grid (splits, KV heads, sequences of the chunk), one wavefront per work-group.
-// Split n_isplits (the last one) is the BF16 sink + window work.
+// Records 0 .. n_isplits-1 are INT2 page ranges, record n_isplits the BF16 sink + window.
 
 template <int G>
 __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
@@ -218,8 +244,11 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
   const DecodeSeq sq = a.seqs[sl];
   const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
-  const int n_isplits = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
-  if (split > n_isplits) return;
+  const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
+  // the BF16 sink + window tokens (partial record n_isplits) ride on the last INT2 split when
+  // it has room for them, else they are work-group n_isplits
+  const bool fold = bf16_folded(sq.n_int2, sq.len, a.pages_per_split, 0);
+  if (split >= n_isplits + (fold ? 0 : 1)) return;
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
                       (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
@@ -228,7 +257,7 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
   // GQA 8: hi 0..15, lo 16..31
   __shared__ _Float16 plds[32][64];
   if (split == n_isplits) {
-    bf16_split<G>(a, sq, kvh, sl, split, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+    bf16_split<G>(a, sq, kvh, sl, n_isplits, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
     return;
   }
 
@@ -472,15 +501,20 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
       }
     }
   }
+  if (fold && split == n_isplits - 1)
+    bf16_split<G>(a, sq, kvh, sl, n_isplits, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
 }
 
+// Work-groups to plan for one residency round: all wave slots of the device but one per
+// compute unit.  Measured on the 100000-token, 32-sequence, 8-KV-head decode: work-groups that
+// fill every slot (12 per CU) ran about 15% slower per page than 11 per CU.
 template <typename K>
 static int resident_for(K kernel, int block) {
   int dev = 0, n_cu = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
-  return n_cu * per_cu;
+  return n_cu * (per_cu > 1 ? per_cu - 1 : 1);
 }
 
 int decode_resident_workgroups(int gqa, int kernel) {
@@ -505,30 +539,29 @@ int decode_resident_workgroups(int gqa, int kernel) {
   return cache[k][gqa];
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
-  const int gqa = a.hq / a.hkv;
-  const dim3 grid(a.n_split_max, a.hkv, a.n_seqs);
-  switch (gqa) {
-    case 1:
-      hipLaunchKernelGGL(k_qprep<1>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_decode_mfma<1>, grid, dim3(64), 0, s, a);
-      break;
-    case 2:
-      hipLaunchKernelGGL(k_qprep<2>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_decode_mfma<2>, grid, dim3(64), 0, s, a);
-      break;
-    case 4:
-      hipLaunchKernelGGL(k_qprep<4>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_decode_mfma<4>, grid, dim3(64), 0, s, a);
-      break;
-    case 8:
-      hipLaunchKernelGGL(k_qprep<8>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_decode_mfma<8>, grid, dim3(64), 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+template <int G>
+static hipError_t launch_g(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+  if (t0) {
+    const hipError_t e = hipEventRecord(t0, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_decode_mfma<G>, dim3(a.n_split_max, a.hkv, a.n_seqs), dim3(64), 0, s, a);
+  if (t1) {
+    const hipError_t e = hipEventRecord(t1, s);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  switch (a.hq / a.hkv) {
+    case 1: return launch_g<1>(a, s, t0, t1);
+    case 2: return launch_g<2>(a, s, t0, t1);
+    case 4: return launch_g<4>(a, s, t0, t1);
+    case 8: return launch_g<8>(a, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace oscar

@@ -73,16 +73,35 @@ struct DecodeArgs {
 
 constexpr int PART_STRIDE = 130;
 
+// Work split of one (sequence, KV head) unit.  INT2 split s covers pages
+// [s pps, min((s+1) pps, n_pages)) and writes partial record s; the BF16 sink + window
+// tokens write record ceil(n_pages / pps).  A BF16 token moves 512 bytes (key and value
+// rows), an INT2 page 5120, so ten BF16 tokens weigh one page.  On the matrix-core path
+// the last INT2 split also does the BF16 work when its spare capacity holds that weight;
+// otherwise the BF16 work is a work-group of its own.
+__host__ __device__ inline int bf16_page_weight(int n_bf16) { return (n_bf16 + 9) / 10; }
+__host__ __device__ inline int int2_splits(int n_int2, int pps) { return ((n_int2 + 63) / 64 + pps - 1) / pps; }
+__host__ __device__ inline bool bf16_folded(int n_int2, int len, int pps, int kernel) {
+  const int n_pages = (n_int2 + 63) / 64, n_is = (n_pages + pps - 1) / pps;
+  return kernel == 0 && n_is > 0 && n_is * pps - n_pages >= bf16_page_weight(len - n_int2);
+}
+// work-groups of the split kernel for one unit
+__host__ __device__ inline int unit_workgroups(int n_int2, int len, int pps, int kernel) {
+  return int2_splits(n_int2, pps) + (bf16_folded(n_int2, len, pps, kernel) ? 0 : 1);
+}
+
 hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s);
+hipError_t launch_append(const WriteArgs& a, hipStream_t s);   // no INT2 tokens in the call
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
 // decode attention: prepared-query + split kernels (matrix-core path) or the reference-grade
 // fp32 kernel, then the split combine
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s);
+// (t0, t1: optional events recorded on s right before and after the split kernel)
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
-// work-groups of the decode split kernel resident on the current device at once
+// work-groups of the decode split kernel to plan per residency round on the current device
 int decode_resident_workgroups(int gqa, int kernel);
 
 // bytes of the prepared-query area that follows the split partials in the workspace,

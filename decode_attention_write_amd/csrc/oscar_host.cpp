@@ -46,6 +46,11 @@ struct oscar_kv {
   int32_t pages_per_split = 0;
   int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
   bool has_rotation = false;
+  std::vector<hipEvent_t> timing_ev;  // 2 * OSCAR_TIMING_PAIRS when timing is on
+  mutable int32_t timing_used = 0;    // pairs recorded since the last read (decode takes a const handle)
+  ~oscar_kv() {
+    for (hipEvent_t e : timing_ev) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -115,7 +120,8 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
   if (kv->pages_per_split > 0) return kv->pages_per_split;
   // Work-groups of the split kernel that fit on the device at once (the matrix-core kernel uses
   // one wavefront per work-group).  Aim for a single residency round holding as many waves as
-  // fit: INT2 splits + one sink/window split per (sequence, KV head) <= resident capacity, for
+  // fit: the smallest pages-per-split whose work-groups (INT2 splits, plus a sink/window
+  // work-group where it is not folded into the last INT2 split) fit the resident capacity, for
   // each launch chunk of up to CHUNK sequences.
   if (kv->plan_only) return 64;
   const int64_t resident = decode_resident_workgroups(kv->desc.num_q_heads / kv->desc.num_kv_heads,
@@ -131,13 +137,19 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
       total += p;
     }
     if (max_pages == 0) continue;
-    const int64_t budget = std::max<int64_t>(n * hkv, resident - n * hkv);
+    const int kernel = kv->decode_kernel;
+    auto wgs_for = [&](int64_t pps) {
+      int64_t w = 0;
+      for (int i = c0; i < c0 + n; ++i) {
+        const int s = seq_ids[i];
+        w += unit_workgroups(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]), static_cast<int>(pps), kernel);
+      }
+      return w * hkv;
+    };
+    const int64_t budget = std::max<int64_t>(n * hkv, resident);
     int64_t pps = std::max<int64_t>(1, ceil_div(total * hkv, budget));
-    for (; pps < max_pages; ++pps) {
-      int64_t wgs = 0;
-      for (int i = c0; i < c0 + n; ++i) wgs += ceil_div(ceil_div(kv->n_int2[seq_ids[i]], kPage), pps);
-      if (wgs * hkv <= budget) break;
-    }
+    for (; pps < max_pages; ++pps)
+      if (wgs_for(pps) <= budget) break;
     best = std::max(best, pps);
   }
   return best;
@@ -300,6 +312,9 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
   rc = push_table(kv, upd, st);
   if (rc) return rc;
   const int n_tiles = static_cast<int>(ceil_div(n_new, kPage));
+  // a call that produces no INT2 token (appends, short first writes) takes the per-token kernel
+  bool any_int2 = false;
+  for (int i = 0; i < n_seqs; ++i) any_int2 |= (plan[i].len0 == 0 && n_new > kRing);
   for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
     WriteArgs a{};
     a.k = static_cast<const uint16_t*>(k);
@@ -313,7 +328,7 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
     a.n_new = n_new;
     a.n_seqs = std::min(CHUNK, n_seqs - c0);
     for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
-    hipError_t e = launch_write(a, n_tiles, st);
+    hipError_t e = any_int2 ? launch_write(a, n_tiles, st) : launch_append(a, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
   }
   return OSCAR_OK;
@@ -432,7 +447,13 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     }
     a.n_split_max = static_cast<int32_t>(max_split);
     a.scale_log2 = sm_scale * 1.4426950408889634f;
-    hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st) : launch_decode_mfma(a, st);
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (!kv->timing_ev.empty() && kv->timing_used < OSCAR_TIMING_PAIRS) {
+      t0 = kv->timing_ev[2 * kv->timing_used];
+      t1 = kv->timing_ev[2 * kv->timing_used + 1];
+      ++kv->timing_used;
+    }
+    hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st, t0, t1) : launch_decode_mfma(a, st, t0, t1);
     if (e == hipSuccess) e = launch_combine(a, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_decode_attn: launch");
   }
@@ -478,6 +499,43 @@ int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, void* stream) {
 int oscar_kv_set_decode_kernel(oscar_kv* kv, int32_t kernel) {
   if (!kv || kernel < 0 || kernel > 1) { set_error("oscar_kv_set_decode_kernel: kernel must be 0 or 1"); return OSCAR_E_ARG; }
   kv->decode_kernel = kernel;
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_decode_timing(oscar_kv* kv, int32_t enable) {
+  if (!kv) { set_error("oscar_kv_set_decode_timing: null handle"); return OSCAR_E_ARG; }
+  if (kv->plan_only) { set_error("oscar_kv_set_decode_timing: plan-only store"); return OSCAR_E_STATE; }
+  for (hipEvent_t ev : kv->timing_ev) (void)hipEventDestroy(ev);
+  kv->timing_ev.clear();
+  kv->timing_used = 0;
+  if (!enable) return OSCAR_OK;
+  std::vector<hipEvent_t> evs(2 * OSCAR_TIMING_PAIRS, nullptr);
+  for (size_t i = 0; i < evs.size(); ++i) {
+    // timing-only events: no system-scope fence (no cache writeback/invalidate around the kernel)
+    const hipError_t e = hipEventCreateWithFlags(&evs[i], hipEventDisableSystemFence);
+    if (e != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(evs[j]);
+      return hip_fail(e, "oscar_kv_set_decode_timing: hipEventCreate");
+    }
+  }
+  kv->timing_ev = std::move(evs);
+  return OSCAR_OK;
+}
+
+int oscar_kv_read_decode_timing(oscar_kv* kv, int32_t* launches, double* total_ms) {
+  if (!kv || !launches || !total_ms) { set_error("oscar_kv_read_decode_timing: null argument"); return OSCAR_E_ARG; }
+  if (kv->timing_ev.empty()) { set_error("oscar_kv_read_decode_timing: timing is off"); return OSCAR_E_STATE; }
+  double sum = 0.0;
+  for (int32_t i = 0; i < kv->timing_used; ++i) {
+    hipError_t e = hipEventSynchronize(kv->timing_ev[2 * i + 1]);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, kv->timing_ev[2 * i], kv->timing_ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "oscar_kv_read_decode_timing");
+    sum += ms;
+  }
+  *launches = kv->timing_used;
+  *total_ms = sum;
+  kv->timing_used = 0;
   return OSCAR_OK;
 }
 

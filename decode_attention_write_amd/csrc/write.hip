@@ -187,6 +187,42 @@ hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ append (no INT2 output)
+// Writes that only reach the BF16 sink / window (every append into a non-empty sequence, and a
+// first write of at most 320 tokens).  Grid (KV heads, sequences of the chunk), 128 threads:
+// thread c owns output channel c of every token; the rotation uses the same fp32 FMA order as
+// the tile kernel above, so both paths store identical bf16 keys.
+
+__global__ __launch_bounds__(128) void k_append(WriteArgs a) {
+  const int kvh = blockIdx.x, sl = blockIdx.y, c = threadIdx.x;
+  const WriteSeq sq = a.seqs[sl];
+  __shared__ float kin[D];
+  const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
+  const size_t row = static_cast<size_t>(a.hkv) * D;
+  const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
+  float rc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) rc[i] = rot[i * D + c];   // column c of R, kept in registers
+  for (int t = 0; t < a.n_new; ++t) {
+    const size_t src = (static_cast<size_t>(sq.src) * a.n_new + t) * row + kvh * D;
+    __syncthreads();
+    kin[c] = bf16_to_f32(a.k[src + c]);
+    __syncthreads();
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
+    const int p = sq.len0 + t;
+    const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
+    a.ring[ring_head + static_cast<size_t>(slot) * D + c] = f32_to_bf16(acc);
+    a.ring[ring_head + static_cast<size_t>(RING + slot) * D + c] = a.v[src + c];
+  }
+}
+
+hipError_t launch_append(const WriteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_append, dim3(a.hkv, a.n_seqs), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ eviction
 // Grid (KV heads, sequences); 256 threads.  Tokens are evicted one after the
 // other: INT2 index i takes ring slot 64 + i % 256 (the oldest window token).

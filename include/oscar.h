@@ -242,6 +242,20 @@ int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);
  * element in fp32 (slow; kept as an independent cross-check). */
 int oscar_kv_set_decode_kernel(oscar_kv *kv, int32_t kernel);
 
+/* Kernel timing (measurement aid).  enable = 1 creates OSCAR_TIMING_PAIRS HIP event
+ * pairs (timing-only: no system-scope fence on record); from then on every oscar_decode_attn call records one pair around each launch
+ * of its split kernel (not the query preparation or the combine), on the call's
+ * stream, until the pairs are used up (further launches go untimed).  enable = 0
+ * destroys the events.  Returns OSCAR_E_ARG on a null handle, OSCAR_E_STATE for a
+ * plan-only store, OSCAR_E_HIP if event creation fails (then timing stays off). */
+#define OSCAR_TIMING_PAIRS 4096
+int oscar_kv_set_decode_timing(oscar_kv *kv, int32_t enable);
+
+/* Waits for the recorded pairs, writes the number of timed launches to *launches
+ * and their summed duration in milliseconds to *total_ms, and frees the pairs for
+ * reuse.  Timing must be on (else OSCAR_E_STATE). */
+int oscar_kv_read_decode_timing(oscar_kv *kv, int32_t *launches, double *total_ms);
+
 const char *oscar_last_error(void);
 void oscar_kv_destroy(oscar_kv *kv);
 

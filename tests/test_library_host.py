@@ -133,3 +133,13 @@ def test_workspace_bytes_and_split_choice():
     nb4 = s.workspace_bytes([0, 1])
     # 20 pages / 4 per split = 5 INT2 splits + 1 BF16 split, 2 seqs x 8 q heads, 130 floats each
     assert nb4 == 2 * 8 * 6 * 130 * 4 + qprep
+
+
+def test_decode_timing_errors():
+    s = _plan_store()
+    with pytest.raises(oscar.OscarError) as e:
+        s.set_decode_timing(True)
+    assert e.value.status == oscar.E_STATE
+    with pytest.raises(oscar.OscarError) as e:
+        s.read_decode_timing()
+    assert e.value.status == oscar.E_STATE
