@@ -146,6 +146,90 @@ def cpu_baseline(units, rots, q_layer0, out_layer0, hq, hkv, total_units, step_b
     }
 
 
+PREFILL_TOKENS, PREFILL_APPENDS = 131072, 1024
+
+
+def prefill_bytes(n_tokens, hkv):
+    """Algorithmic bytes of a first write of n_tokens: bf16 K and V read (512 B per token-head),
+    INT2 written (80 B per INT2 token-head), BF16 written (512 B per sink/window token-head),
+    page ids written."""
+    n_bf16 = min(n_tokens, 320)
+    n_int2 = n_tokens - n_bf16
+    return hkv * (512 * n_tokens + 80 * n_int2 + 512 * n_bf16) + 4 * (-(-n_int2 // 64))
+
+
+def prefill_leg(reps=5):
+    """One 131072-token sequence x 8 KV heads: the multi-token write (rotation on the matrix cores,
+    clip, INT2, pack), then 1024 sequential single-token appends each evicting one window token."""
+    import numpy as np
+    import torch
+
+    import decode_attention_write_amd as oscar
+    import synth
+    from synth import gpu as sgpu
+
+    cfg, hkv, hq, L = synth.CFG_PREFILL, 8, 32, PREFILL_TOKENS
+    rots = np.stack([oscar.oscar_calibrate_host(synth.bf16_bits_to_f32(synth.calibration_queries(cfg, 0, h)))[0]
+                     for h in range(hkv)])
+    max_pages = -(-(L + PREFILL_APPENDS) // 64) + 1
+    st = oscar.KVStore(hq, hkv, 1, max_pages, max_pages, free_pages=synth.page_permutation(cfg, 0, max_pages))
+    st.set_rotation(rots)
+    prm = sgpu.HeadParams(cfg, 0, hkv)
+    kbuf = torch.empty((1, L + PREFILL_APPENDS, hkv, 128), dtype=torch.int16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    sgpu.draw_kv(prm, 0, 0, L + PREFILL_APPENDS, kbuf[0], vbuf[0])
+    kpre, vpre = kbuf[:, :L], vbuf[:, :L]
+    st.set_timing(True)
+    call_ms = []
+    for r in range(reps + 1):
+        st.reset_seq(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        st.write([0], kpre, vpre)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            call_ms.append(e0.elapsed_time(e1))
+    n, k_ms = st.read_timing(oscar.TIMED_WRITE)
+    assert n == reps + 1, n
+    kernel_us = k_ms * 1e3 / n
+    nbytes = prefill_bytes(L, hkv)
+    # algorithmic matrix-core work: k . R_K per token-head (2 * 128 * 128 flop); the kernel runs
+    # it three times (bf16 terms r0 + r1 + r2 of R_K)
+    flop = 2 * 128 * 128 * L * hkv
+    # appends: evict the oldest window token into INT2, then write one token, per step
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for i in range(PREFILL_APPENDS):
+        st.evict([0], 1)
+        st.write([0], kbuf[:, L + i:L + i + 1], vbuf[:, L + i:L + i + 1])
+    a1.record()
+    torch.cuda.synchronize()
+    st.set_timing(False)
+    append_us = a0.elapsed_time(a1) * 1e3 / PREFILL_APPENDS
+    assert st.seq_info(0) == (L + PREFILL_APPENDS, L + PREFILL_APPENDS - 320)
+    res = {
+        "workload": f"prefill write: 1 sequence x {L} tokens x {hkv} KV heads (bf16 K/V in, INT2 pages + "
+                    f"BF16 sink/window out), then {PREFILL_APPENDS} single-token appends each evicting one",
+        "call_us": round(float(np.median(call_ms)) * 1e3, 2),
+        "kernel_us": round(kernel_us, 2),
+        "bytes": nbytes,
+        "gbps_kernel": round(nbytes / kernel_us / 1e3, 1),
+        "gbps_call": round(nbytes / (float(np.median(call_ms)) * 1e3) / 1e3, 1),
+        "pct_peak_kernel": round(100 * nbytes / kernel_us / 1e3 / PEAK_GBPS, 2),
+        "rotation_tflops_algorithmic": round(flop / kernel_us / 1e6, 1),
+        "rotation_mfma_frac_executed": round(3 * flop / kernel_us / 1e6 / 2500.0, 4),
+        "append_step_us": round(append_us, 2),
+    }
+    log(f"prefill: call {res['call_us']} us, write kernel {res['kernel_us']} us = {res['gbps_kernel']} GB/s "
+        f"({res['pct_peak_kernel']}% of 8 TB/s); rotation {res['rotation_tflops_algorithmic']} TFLOP/s algorithmic; "
+        f"evict+append step {res['append_step_us']} us")
+    del kbuf, vbuf, st
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +243,7 @@ def main():
                     help="run a plain device copy of this size at the end (counter scaling in profiled runs)")
     ap.add_argument("--cpu-units", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 131072-token prefill-write leg")
     ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
     ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
@@ -311,7 +396,7 @@ def main():
         info = [st.seq_info(s) for s in seqs]
         kbytes.append(split_kernel_bytes([L for L, _ in info], [n2 for _, n2 in info], hkv))
     for st in stores:
-        st.set_decode_timing(True)
+        st.set_timing(True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
     for r in range(args.attn_reps):
         for l, st in enumerate(stores):
@@ -322,10 +407,10 @@ def main():
         per_call.extend(a.elapsed_time(b) for a, b in evs)
     k_launches, k_ms = 0, 0.0
     for st in stores:
-        n, ms = st.read_decode_timing()
+        n, ms = st.read_timing(oscar.TIMED_DECODE)
         k_launches += n
         k_ms += ms
-        st.set_decode_timing(False)
+        st.set_timing(False)
     n_chunks = -(-B // 64)
     assert k_launches == args.attn_reps * n_layers * n_chunks, k_launches
     kernel_us = k_ms * 1e3 / k_launches
@@ -373,6 +458,8 @@ def main():
             "bytes_per_launch": int(kernel_bytes),
         },
     }
+    if not args.no_prefill:
+        result["prefill"] = prefill_leg()
     if args.copy_calib_mib:
         # a plain copy of known size, for scaling the memory counters of a profiled run
         n = args.copy_calib_mib * (1 << 20) // 4

@@ -29,6 +29,7 @@ HEAD_BLOCK = 5120
 FLAG_PLAN_ONLY = 1
 
 OK, E_ARG, E_NOPAGE, E_WINDOW_FULL, E_WINDOW_SHORT, E_NUMERIC, E_HIP, E_WORKSPACE, E_STATE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+TIMED_DECODE, TIMED_WRITE = 0, 1  # kernels recorded by KVStore.set_timing
 _NAMES = {E_ARG: "E_ARG", E_NOPAGE: "E_NOPAGE", E_WINDOW_FULL: "E_WINDOW_FULL", E_WINDOW_SHORT: "E_WINDOW_SHORT",
           E_NUMERIC: "E_NUMERIC", E_HIP: "E_HIP", E_WORKSPACE: "E_WORKSPACE", E_STATE: "E_STATE"}
 
@@ -36,8 +37,8 @@ EXPORTS = [
     "oscar_calibrate_host", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
-    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_decode_timing",
-    "oscar_kv_read_decode_timing", "oscar_last_error", "oscar_kv_destroy",
+    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_timing",
+    "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
 ]
 
 
@@ -82,8 +83,8 @@ def load():
         "oscar_kv_reset_seq": [P, I32, P],
         "oscar_kv_set_decode_split": [P, I32],
         "oscar_kv_set_decode_kernel": [P, I32],
-        "oscar_kv_set_decode_timing": [P, I32],
-        "oscar_kv_read_decode_timing": [P, P, P],
+        "oscar_kv_set_timing": [P, I32],
+        "oscar_kv_read_timing": [P, I32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -258,15 +259,17 @@ class KVStore:
         """0 = matrix-core kernel (default), 1 = reference-grade fp32 kernel."""
         _check(load().oscar_kv_set_decode_kernel(self.handle, int(kernel)))
 
-    def set_decode_timing(self, enable=True):
-        """Record HIP events around every launch of the decode split kernel (measurement aid)."""
-        _check(load().oscar_kv_set_decode_timing(self.handle, int(bool(enable))))
+    def set_timing(self, enable=True):
+        """Record HIP events around every launch of the decode split kernel and the write kernel
+        (measurement aid)."""
+        _check(load().oscar_kv_set_timing(self.handle, int(bool(enable))))
 
-    def read_decode_timing(self):
-        """(timed launches, summed split-kernel milliseconds) since the last read; waits for them."""
+    def read_timing(self, kernel):
+        """(timed launches, summed milliseconds) of TIMED_DECODE or TIMED_WRITE since the last
+        read of that kernel; waits for them."""
         n = ctypes.c_int32(0)
         ms = ctypes.c_double(0.0)
-        _check(load().oscar_kv_read_decode_timing(self.handle, ctypes.byref(n), ctypes.byref(ms)))
+        _check(load().oscar_kv_read_timing(self.handle, int(kernel), ctypes.byref(n), ctypes.byref(ms)))
         return n.value, ms.value
 
     # ---- views of the device buffers (for tests and export)

@@ -27,6 +27,8 @@
 // Each wavefront walks the pages of one (sequence, KV head, split) with 128-bit loads
 // of the raw page block, keeps a running softmax max (rescaling only when a new max
 // appears), and writes an (m, l, o) partial for the split combine.
+#include <type_traits>
+
 #include "common.h"
 
 namespace oscar {
@@ -137,7 +139,7 @@ __device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 // Exponent e of the f16 denormal a value code lands in, by its position p' = 4 s + kk/2
 // within the 32-bit word (see the unpack in the page loop).
 __device__ inline int vcode_exp(int p) {
-  constexpr int E[8] = {4, 6, 4, 6, 8, 4, 6, 8};
+  constexpr int E[8] = {0, 2, 4, 6, 8, 4, 6, 8};
   return E[p];
 }
 
@@ -237,7 +239,8 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
 // Records 0 .. n_isplits-1 are INT2 page ranges, record n_isplits the BF16 sink + window.
 
 template <int G>
-__global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
+// Occupancy target: 3 waves per SIMD (2 for GQA 8, whose P.V needs twice the operands).
+__global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a) {
   constexpr int GP = G < 4 ? 4 : G;       // heads padded to a multiple of 4
   constexpr int HB = GP / 4;              // head blocks (MFMA row blocks of Q.K)
   const int split = blockIdx.x, kvh = blockIdx.y, sl = blockIdx.z;
@@ -261,13 +264,14 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
     return;
   }
 
-  // ---- prologue: query operands and per-head constants
-  v4i aop[HB][2];
+  // ---- prologue: query operands (kept in LDS and read per page, which leaves the registers
+  // for a third page buffer) and per-head constants
+  __shared__ v4i aop_lds[HB][2][64];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int g = 0; g < 2; ++g)
-      aop[hb][g] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + ((hb * 64 + lane) * 2 + g) * 16);
+      aop_lds[hb][g][lane] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + ((hb * 64 + lane) * 2 + g) * 16);
   // per-head constants are wave-uniform: keep them in scalar registers
   float cst[G][3];
   const float* wc = reinterpret_cast<const float*>(ws + QP_CONST);
@@ -300,18 +304,17 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
   __syncthreads();
 
   // Raw page block (128-bit loads): key codes (2 per lane), value codes (2 per lane), and the
-  // metadata of this lane's token.  Pages are loaded one ahead into two register sets that
-  // alternate, always issuing the next load (clamped to the last page) so the wait counts stay
-  // exact.  Page ids come from a 64-entry vector of the page-table row via readlane.
+  // metadata of this lane's token.  Pages are loaded ahead into rotating register sets, always
+  // issuing the next load (clamped to the last page) so the wait counts stay exact.  Page ids
+  // are scalar loads through the constant address space, fetched one page ahead: they wait on
+  // the scalar/LDS counter, so no wait on the vector-memory counter ever drains the prefetch.
   struct Raw { v4u kc0, kc1, vc0, vc1, md; };
-  int pbase = first;
-  int pvec = ptab[min(first + lane, max(first, last - 1))];
+  const __attribute__((address_space(4))) int32_t* ptab_c =
+      (const __attribute__((address_space(4))) int32_t*)(ptab);
+  int id_next = ptab_c[first];
   auto load_page = [&](int lpn, Raw& r) {
-    if (lpn - pbase >= 64) {
-      pbase += 64;
-      pvec = ptab[min(pbase + lane, last - 1)];
-    }
-    const int page = __builtin_amdgcn_readlane(pvec, lpn - pbase);
+    const int page = id_next;
+    id_next = ptab_c[min(lpn + 1, last - 1)];
     const uint8_t* blk = a.pool + static_cast<size_t>(page) * page_stride + head_off;
     const v4u* kp = reinterpret_cast<const v4u*>(blk + KC_OFF) + lane;
     const v4u* vp = reinterpret_cast<const v4u*>(blk + VC_OFF) + lane;
@@ -322,7 +325,9 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
     r.md = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(blk + META_OFF) + tok);
   };
 
-  auto process_page = [&](int lp, const Raw& raw) {
+  // FULL (a compile-time tag): every token of the page holds a code, so no per-token masking
+  auto process_page = [&](int lp, const Raw& raw, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const v4u& kc0 = raw.kc0;
     const v4u& kc1 = raw.kc1;
     const v4u& vc0 = raw.vc0;
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
           if (g == 0) acc[hb][t] = v4i{0, 0, 0, 0};
-          acc[hb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[hb][g], b, acc[hb][t], 0, 0, 0);
+          acc[hb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop_lds[hb][g][lane], b, acc[hb][t], 0, 0, 0);
         }
       }
     }
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
     const float lk0 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.x >> 16)));
     const float sk1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.y & 0xFFFF)));
     const float lk1 = __half2float(__ushort_as_half(static_cast<unsigned short>(md.y >> 16)));
-    const bool valid = tok < n_valid;
+    const bool valid = FULL || tok < n_valid;
     float z[G];
     float zmax = -INFINITY;
 #pragma unroll
@@ -439,8 +444,8 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const uint32_t w = (ct < 4) ? vc0[ct & 3] : vc1[ct & 3];
-      const uint32_t lo4 = w << 4, hi6 = w >> 6;
-      const v8h b0 = as_h8(lo4 & 0x00300030u, lo4 & 0x00C000C0u, w & 0x00300030u, w & 0x00C000C0u);
+      const uint32_t hi6 = w >> 6;
+      const v8h b0 = as_h8(w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u);
       const v8h b1 = as_h8(w & 0x03000300u, hi6 & 0x00300030u, hi6 & 0x00C000C0u, hi6 & 0x03000300u);
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA0, b0, oacc[ct], 0, 0, 0);
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA1, b1, oacc[ct], 0, 0, 0);
@@ -452,14 +457,55 @@ __global__ __launch_bounds__(64) void k_decode_mfma(DecodeArgs a) {
   };
 
   if (first < last) {
-    Raw bx, by;
-    load_page(first, bx);
-    for (int lp = first; lp < last; lp += 2) {
-      load_page(min(lp + 1, last - 1), by);
-      process_page(lp, bx);
-      if (lp + 1 >= last) break;
-      load_page(min(lp + 2, last - 1), bx);
-      process_page(lp + 1, by);
+    // NBUF rotating register sets: NBUF - 1 pages in flight while one is processed (two for
+    // GQA <= 4; one for GQA 8, whose registers are taken by its wider P.V operands)
+    // pages [first, last_full) are full; a partially filled last page of the sequence is
+    // handled after the main loop, with masking
+    const int last_full = (last == n_pages && (sq.n_int2 % PAGE) != 0) ? last - 1 : last;
+    const std::true_type full{};
+    const std::false_type masked{};
+    if constexpr (G == 8) {
+      Raw b0, b1;
+      load_page(first, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      int lp = first;
+      for (; lp + 2 <= last_full; lp += 2) {
+        load_page(lp + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
+        process_page(lp, b0, full);
+        load_page(min(lp + 2, last - 1), b0);
+        __builtin_amdgcn_sched_barrier(0);
+        process_page(lp + 1, b1, full);
+      }
+      // at most one full page and the partial page left; b0 holds page lp
+      if (lp + 1 < last) load_page(lp + 1, b1);
+      if (lp < last) process_page(lp, b0, masked);
+      if (lp + 1 < last) process_page(lp + 1, b1, masked);
+    } else {
+      Raw b0, b1, b2;
+      load_page(first, b0);
+      __builtin_amdgcn_sched_barrier(0);  // keep page order in the queue: waits stay vmcnt(10)
+      load_page(min(first + 1, last - 1), b1);
+      __builtin_amdgcn_sched_barrier(0);
+      int lp = first;
+      for (; lp + 3 <= last_full; lp += 3) {
+        load_page(lp + 2, b2);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
+        process_page(lp, b0, full);
+        load_page(min(lp + 3, last - 1), b0);
+        __builtin_amdgcn_sched_barrier(0);
+        process_page(lp + 1, b1, full);
+        load_page(min(lp + 4, last - 1), b1);
+        __builtin_amdgcn_sched_barrier(0);
+        process_page(lp + 2, b2, full);
+      }
+      // up to two full pages and the partial page left; b0 and b1 hold pages lp and lp + 1
+      // (the loop has no early exit: an exit edge would merge wait states and force a full
+      // drain of the prefetch at the loop head)
+      if (lp < last) process_page(lp, b0, masked);
+      if (lp + 2 < last) load_page(lp + 2, b0);   // b0 is free again: two register sets suffice
+      if (lp + 1 < last) process_page(lp + 1, b1, masked);
+      if (lp + 2 < last) process_page(lp + 2, b0, masked);
     }
   }
 

@@ -11,6 +11,14 @@ namespace oscar {
 constexpr int CHUNK = 64;          // sequences per launch
 constexpr int SCATTER_MAX = 224;   // page-table updates per scatter launch
 
+// A run of consecutive page-table entries (one sequence's new pages) in one launch.
+constexpr int RUN_MAX = 1000;
+struct RunArgs {
+  int32_t* dst;   // first entry of the run
+  int32_t n;
+  int32_t val[RUN_MAX];
+};
+
 struct ScatterArgs {
   int32_t* dst;
   int32_t n;
@@ -92,6 +100,7 @@ __host__ __device__ inline int unit_workgroups(int n_int2, int len, int pps, int
 
 hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
+hipError_t launch_run(const RunArgs& a, hipStream_t s);
 hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s);
 hipError_t launch_append(const WriteArgs& a, hipStream_t s);   // no INT2 tokens in the call
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s);

@@ -46,10 +46,18 @@ struct oscar_kv {
   int32_t pages_per_split = 0;
   int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
   bool has_rotation = false;
-  std::vector<hipEvent_t> timing_ev;  // 2 * OSCAR_TIMING_PAIRS when timing is on
-  mutable int32_t timing_used = 0;    // pairs recorded since the last read (decode takes a const handle)
+  // timing events per timed kernel: 2 * OSCAR_TIMING_PAIRS each when timing is on
+  std::vector<hipEvent_t> timing_ev[2];
+  mutable int32_t timing_used[2] = {0, 0};  // pairs recorded since the last read (decode takes a const handle)
   ~oscar_kv() {
-    for (hipEvent_t e : timing_ev) (void)hipEventDestroy(e);
+    for (auto& v : timing_ev)
+      for (hipEvent_t e : v) (void)hipEventDestroy(e);
+  }
+  // next free event pair of a timed kernel, or {null, null}
+  std::pair<hipEvent_t, hipEvent_t> take_timing_pair(int kind) const {
+    if (timing_ev[kind].empty() || timing_used[kind] >= OSCAR_TIMING_PAIRS) return {nullptr, nullptr};
+    const int i = timing_used[kind]++;
+    return {timing_ev[kind][2 * i], timing_ev[kind][2 * i + 1]};
   }
 };
 
@@ -99,16 +107,35 @@ int check_seqs(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-// Push page-table updates to the device in scatter launches.
+// Push page-table updates to the device: runs of at least 64 consecutive entries (a long write
+// into one sequence) go in run launches of up to RUN_MAX values, the rest in scatter launches.
 int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd, hipStream_t st) {
   if (kv->plan_only || upd.empty()) return OSCAR_OK;
-  for (size_t i = 0; i < upd.size(); i += SCATTER_MAX) {
+  std::vector<std::pair<int32_t, int32_t>> rest;
+  for (size_t i = 0; i < upd.size();) {
+    size_t j = i + 1;
+    while (j < upd.size() && upd[j].first == upd[j - 1].first + 1) ++j;
+    if (j - i >= 64) {
+      for (size_t r = i; r < j; r += RUN_MAX) {
+        RunArgs a{};
+        a.dst = kv->desc.page_table + upd[r].first;
+        a.n = static_cast<int32_t>(std::min<size_t>(RUN_MAX, j - r));
+        for (int k = 0; k < a.n; ++k) a.val[k] = upd[r + k].second;
+        hipError_t e = launch_run(a, st);
+        if (e != hipSuccess) return hip_fail(e, "page-table update");
+      }
+    } else {
+      rest.insert(rest.end(), upd.begin() + i, upd.begin() + j);
+    }
+    i = j;
+  }
+  for (size_t i = 0; i < rest.size(); i += SCATTER_MAX) {
     ScatterArgs a{};
     a.dst = kv->desc.page_table;
-    a.n = static_cast<int32_t>(std::min<size_t>(SCATTER_MAX, upd.size() - i));
+    a.n = static_cast<int32_t>(std::min<size_t>(SCATTER_MAX, rest.size() - i));
     for (int k = 0; k < a.n; ++k) {
-      a.idx[k] = upd[i + k].first;
-      a.val[k] = upd[i + k].second;
+      a.idx[k] = rest[i + k].first;
+      a.val[k] = rest[i + k].second;
     }
     hipError_t e = launch_scatter(a, st);
     if (e != hipSuccess) return hip_fail(e, "page-table update");
@@ -219,7 +246,8 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
   for (size_t i = 0; i < n; ++i)
     if (!std::isfinite(rot_host[i])) { set_error("oscar_kv_set_rotation: non-finite entry"); return OSCAR_E_NUMERIC; }
   if (kv->plan_only) { kv->has_rotation = true; return OSCAR_OK; }
-  // per head: fp32 R, then three bf16 terms r0 + r1 + r2 ~= R (each the bf16 rounding of the remainder)
+  // per head: fp32 R, then three bf16 terms r0 + r1 + r2 ~= R (each the bf16 rounding of the
+  // remainder), stored transposed ([term][output channel c][input channel i]) for the MFMA A operand
   std::vector<uint8_t> blob(static_cast<size_t>(hkv) * OSCAR_ROT_HEAD_BYTES);
   const size_t dd = OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
   auto to_bf16 = [](float x) -> uint16_t {
@@ -238,14 +266,15 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
     uint8_t* base = blob.data() + static_cast<size_t>(h) * OSCAR_ROT_HEAD_BYTES;
     std::memcpy(base, rot_host + h * dd, dd * 4);
     uint16_t* terms = reinterpret_cast<uint16_t*>(base + dd * 4);
-    for (size_t i = 0; i < dd; ++i) {
-      float rem = rot_host[h * dd + i];
-      for (int t = 0; t < 3; ++t) {
-        const uint16_t b = to_bf16(rem);
-        terms[t * dd + i] = b;
-        rem = rem - from_bf16(b);
+    for (size_t i = 0; i < OSCAR_HEAD_DIM; ++i)
+      for (size_t c = 0; c < OSCAR_HEAD_DIM; ++c) {
+        float rem = rot_host[h * dd + i * OSCAR_HEAD_DIM + c];
+        for (int t = 0; t < 3; ++t) {
+          const uint16_t b = to_bf16(rem);
+          terms[t * dd + c * OSCAR_HEAD_DIM + i] = b;
+          rem = rem - from_bf16(b);
+        }
       }
-    }
   }
   hipError_t e = hipMemcpyAsync(kv->desc.rot, blob.data(), blob.size(), hipMemcpyHostToDevice, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "oscar_kv_set_rotation: upload");
@@ -328,7 +357,10 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
     a.n_new = n_new;
     a.n_seqs = std::min(CHUNK, n_seqs - c0);
     for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
-    hipError_t e = any_int2 ? launch_write(a, n_tiles, st) : launch_append(a, st);
+    const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_WRITE);
+    hipError_t e = t0 ? hipEventRecord(t0, st) : hipSuccess;
+    if (e == hipSuccess) e = any_int2 ? launch_write(a, n_tiles, st) : launch_append(a, st);
+    if (e == hipSuccess && t1) e = hipEventRecord(t1, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
   }
   return OSCAR_OK;
@@ -447,12 +479,7 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     }
     a.n_split_max = static_cast<int32_t>(max_split);
     a.scale_log2 = sm_scale * 1.4426950408889634f;
-    hipEvent_t t0 = nullptr, t1 = nullptr;
-    if (!kv->timing_ev.empty() && kv->timing_used < OSCAR_TIMING_PAIRS) {
-      t0 = kv->timing_ev[2 * kv->timing_used];
-      t1 = kv->timing_ev[2 * kv->timing_used + 1];
-      ++kv->timing_used;
-    }
+    const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
     hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st, t0, t1) : launch_decode_mfma(a, st, t0, t1);
     if (e == hipSuccess) e = launch_combine(a, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_decode_attn: launch");
@@ -502,40 +529,51 @@ int oscar_kv_set_decode_kernel(oscar_kv* kv, int32_t kernel) {
   return OSCAR_OK;
 }
 
-int oscar_kv_set_decode_timing(oscar_kv* kv, int32_t enable) {
-  if (!kv) { set_error("oscar_kv_set_decode_timing: null handle"); return OSCAR_E_ARG; }
-  if (kv->plan_only) { set_error("oscar_kv_set_decode_timing: plan-only store"); return OSCAR_E_STATE; }
-  for (hipEvent_t ev : kv->timing_ev) (void)hipEventDestroy(ev);
-  kv->timing_ev.clear();
-  kv->timing_used = 0;
-  if (!enable) return OSCAR_OK;
-  std::vector<hipEvent_t> evs(2 * OSCAR_TIMING_PAIRS, nullptr);
-  for (size_t i = 0; i < evs.size(); ++i) {
-    // timing-only events: no system-scope fence (no cache writeback/invalidate around the kernel)
-    const hipError_t e = hipEventCreateWithFlags(&evs[i], hipEventDisableSystemFence);
-    if (e != hipSuccess) {
-      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(evs[j]);
-      return hip_fail(e, "oscar_kv_set_decode_timing: hipEventCreate");
-    }
+int oscar_kv_set_timing(oscar_kv* kv, int32_t enable) {
+  if (!kv) { set_error("oscar_kv_set_timing: null handle"); return OSCAR_E_ARG; }
+  if (kv->plan_only) { set_error("oscar_kv_set_timing: plan-only store"); return OSCAR_E_STATE; }
+  for (int k = 0; k < 2; ++k) {
+    for (hipEvent_t ev : kv->timing_ev[k]) (void)hipEventDestroy(ev);
+    kv->timing_ev[k].clear();
+    kv->timing_used[k] = 0;
   }
-  kv->timing_ev = std::move(evs);
+  if (!enable) return OSCAR_OK;
+  for (int k = 0; k < 2; ++k) {
+    std::vector<hipEvent_t> evs(2 * OSCAR_TIMING_PAIRS, nullptr);
+    for (size_t i = 0; i < evs.size(); ++i) {
+      // timing-only events: no system-scope fence (no cache writeback/invalidate around the kernel)
+      const hipError_t e = hipEventCreateWithFlags(&evs[i], hipEventDisableSystemFence);
+      if (e != hipSuccess) {
+        for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(evs[j]);
+        if (k == 1) {
+          for (hipEvent_t ev : kv->timing_ev[0]) (void)hipEventDestroy(ev);
+          kv->timing_ev[0].clear();
+        }
+        return hip_fail(e, "oscar_kv_set_timing: hipEventCreate");
+      }
+    }
+    kv->timing_ev[k] = std::move(evs);
+  }
   return OSCAR_OK;
 }
 
-int oscar_kv_read_decode_timing(oscar_kv* kv, int32_t* launches, double* total_ms) {
-  if (!kv || !launches || !total_ms) { set_error("oscar_kv_read_decode_timing: null argument"); return OSCAR_E_ARG; }
-  if (kv->timing_ev.empty()) { set_error("oscar_kv_read_decode_timing: timing is off"); return OSCAR_E_STATE; }
+int oscar_kv_read_timing(oscar_kv* kv, int32_t kernel, int32_t* launches, double* total_ms) {
+  if (!kv || !launches || !total_ms || kernel < 0 || kernel > 1) {
+    set_error("oscar_kv_read_timing: null argument or unknown kernel");
+    return OSCAR_E_ARG;
+  }
+  if (kv->timing_ev[kernel].empty()) { set_error("oscar_kv_read_timing: timing is off"); return OSCAR_E_STATE; }
   double sum = 0.0;
-  for (int32_t i = 0; i < kv->timing_used; ++i) {
-    hipError_t e = hipEventSynchronize(kv->timing_ev[2 * i + 1]);
+  for (int32_t i = 0; i < kv->timing_used[kernel]; ++i) {
+    hipError_t e = hipEventSynchronize(kv->timing_ev[kernel][2 * i + 1]);
     float ms = 0.0f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, kv->timing_ev[2 * i], kv->timing_ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_fail(e, "oscar_kv_read_decode_timing");
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, kv->timing_ev[kernel][2 * i], kv->timing_ev[kernel][2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "oscar_kv_read_timing");
     sum += ms;
   }
-  *launches = kv->timing_used;
+  *launches = kv->timing_used[kernel];
   *total_ms = sum;
-  kv->timing_used = 0;
+  kv->timing_used[kernel] = 0;
   return OSCAR_OK;
 }
 

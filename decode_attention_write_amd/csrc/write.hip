@@ -22,10 +22,20 @@ __global__ void k_scatter(ScatterArgs a) {
   if (i < a.n) a.dst[a.idx[i]] = a.val[i];
 }
 
+__global__ void k_run(RunArgs a) {
+  for (int i = threadIdx.x; i < a.n; i += blockDim.x) a.dst[i] = a.val[i];
+}
+
 hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(k_fill_i32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dst, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_run(const RunArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_run, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -35,163 +45,210 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ packing helpers
-
-// Pack a 64-token head block from per-token codes (LDS bytes, one per code) and
-// metadata halves.  256 threads; every word of the block is written, so slots
-// without a token (codes 0, metadata 0) come out zero.
-__device__ inline void pack_block(uint32_t* blk, const uint8_t (*kc)[D], const uint8_t (*vc)[D],
-                                  const uint16_t (*meta)[8], int tid) {
-  for (int w = tid; w < 512; w += 256) {
-    // key word w: inverse of kc_word
-    const int t2 = w >> 8, lane = (w & 255) >> 2, d = w & 3;
-    const int t = 2 * t2 + (d >> 1), g = d & 1, kq = lane >> 4, n = lane & 15;
-    const int j = 16 * t + n;
-    uint32_t word = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int c = 64 * g + 16 * kq + u;
-      word |= static_cast<uint32_t>(kc[j][c]) << kc_bit(c);
-    }
-    blk[(KC_OFF >> 2) + w] = word;
-  }
-  for (int w = tid; w < 512; w += 256) {
-    // value word w: inverse of vc_word
-    const int ct = 4 * (w >> 8) + (w & 3), lane = (w & 255) >> 2;
-    const int kq = lane >> 4, n = lane & 15, c = 16 * ct + n;
-    uint32_t word = 0;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int j = 32 * s + 8 * kq + kk;
-        word |= static_cast<uint32_t>(vc[j][c]) << vc_bit(j);
-      }
-    blk[(VC_OFF >> 2) + w] = word;
-  }
-  {
-    const int w = tid;  // 256 metadata words: token w/4, halves 2*(w%4), 2*(w%4)+1
-    const int j = w >> 2, h = 2 * (w & 3);
-    blk[(META_OFF >> 2) + w] = static_cast<uint32_t>(meta[j][h]) | (static_cast<uint32_t>(meta[j][h + 1]) << 16);
-  }
-}
-
 // ------------------------------------------------------------------ write kernel
-// Grid (tiles of 64 positions, KV heads, sequences of this chunk); 256 threads.
-// Tile i covers positions len0 + 64 i ... of its sequence.  For a sequence that
-// was empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.
+// Grid (groups of WRITE_TILES tiles of 64 positions, KV heads, sequences of this chunk); 256
+// threads.  Tile i covers positions len0 + 64 i ... of its sequence.  For a sequence that was
+// empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.
+//
+// Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_bf16.  The
+// A operand is R^T as three bf16 terms (r0 + r1 + r2 = R to fp32 precision), the B operand the
+// bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
+// its R^T operands in registers for all tiles of the work-group.
 
-__global__ __launch_bounds__(256) void k_write(WriteArgs a) {
-  const int tile = blockIdx.x, kvh = blockIdx.y, sl = blockIdx.z;
-  const int tid = threadIdx.x;
+constexpr int WRITE_TILES = 4;
+constexpr int XS = D + 4;  // fp32 row stride of the rotated tile (16-byte aligned rows)
+constexpr int KS = D + 8;  // bf16 row stride of the key tile
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f_w __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u_w __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
+  const int kvh = blockIdx.y, sl = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, n16 = lane & 15;
   const WriteSeq sq = a.seqs[sl];
-  const int n_here = min(PAGE, a.n_new - tile * PAGE);
-  if (n_here <= 0) return;
-  const int p0 = sq.len0 + tile * PAGE;
+  const int n_tiles = (a.n_new + PAGE - 1) / PAGE;
+  const int tile0 = blockIdx.x * WRITE_TILES;
+  if (tile0 >= n_tiles) return;
+  const int tile1 = min(tile0 + WRITE_TILES, n_tiles);
   const int len = sq.len0 + a.n_new;
   const int n_int2 = (sq.len0 == 0) ? max(0, len - RING) : 0;  // INT2 tokens of this call
 
-  // kin (rotation input) and the code arrays (quantizer output) are never live together
-  __shared__ union {
-    uint16_t kin[PAGE][D];                 // bf16 keys of the tile
-    struct {
-      uint8_t kc[PAGE][D];
-      uint8_t vc[PAGE][D];
-    } q;
-  } sm;
-  __shared__ float x[PAGE][D + 1];         // rotated keys, fp32
-  __shared__ uint16_t meta[PAGE][8];
-  uint16_t (*kin)[D] = sm.kin;
-  uint8_t (*kc)[D] = sm.q.kc;
-  uint8_t (*vc)[D] = sm.q.vc;
+  // The tile buffer holds the bf16 keys (rotation input), then the bf16 values (quantizer input).
+  __shared__ uint16_t tin[PAGE][KS];
+  __shared__ float x[PAGE][XS];            // rotated keys, fp32
+  // value quantizer parameters per (token, group): fp32 minimum and reciprocal scale
+  __shared__ float qlo[PAGE][2], qinv[PAGE][2];
+
+  // A operands: R^T rows of this wave's output channels, 4 K-steps of 32 input channels, 3 terms
+  const uint16_t* terms = reinterpret_cast<const uint16_t*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES + D * D * 4);
+  v8bf aop[2][4][3];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        aop[mt][ks][t] = *reinterpret_cast<const v8bf*>(terms + t * D * D + (32 * wave + 16 * mt + n16) * D + 32 * ks + 8 * q4);
 
   const size_t row = static_cast<size_t>(a.hkv) * D;
-  const uint16_t* ksrc = a.k + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
-  const uint16_t* vsrc = a.v + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
-  for (int i = tid; i < PAGE * D; i += 256) {
-    const int j = i / D, c = i % D;
-    kin[j][c] = (j < n_here) ? ksrc[static_cast<size_t>(j) * row + c] : 0;
-  }
-  __syncthreads();
-
-  // rotation x = k . R (fp32, VALU): thread owns channel c for 32 tokens
-  {
-    const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
-    const int c = tid & (D - 1), jh = tid >> 7;
-    float acc[32];
-#pragma unroll
-    for (int t = 0; t < 32; ++t) acc[t] = 0.0f;
-    for (int i = 0; i < D; ++i) {
-      const float r = rot[i * D + c];
-#pragma unroll
-      for (int t = 0; t < 32; ++t) acc[t] = fmaf(bf16_to_f32(kin[2 * t + jh][i]), r, acc[t]);
-    }
-#pragma unroll
-    for (int t = 0; t < 32; ++t) x[2 * t + jh][c] = acc[t];
-  }
-  __syncthreads();
-
-  // BF16 destinations: sink / window
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
-  for (int i = tid; i < n_here * D; i += 256) {
-    const int j = i / D, c = i % D, p = p0 + j;
-    const bool int2 = (p >= SINK) && (p < SINK + n_int2);
-    if (int2) continue;
-    const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
-    a.ring[ring_head + static_cast<size_t>(slot) * D + c] = f32_to_bf16(x[j][c]);
-    a.ring[ring_head + static_cast<size_t>(RING + slot) * D + c] = vsrc[static_cast<size_t>(j) * row + c];
-  }
-
-  // INT2 destination: tokens j with SINK <= p0 + j < SINK + n_int2 (tile >= 1 of an empty sequence)
-  int n_q = 0;
-  if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
-  if (n_q == 0) return;  // uniform across the block
-
-  {
-    // one (token, group, K/V) task per thread
-    const int j = tid & 63, g = (tid >> 6) & 1, isv = tid >> 7;
-    float mn = 0.0f, mx = 0.0f;
-    float vals[GROUP];
-    if (j < n_q) {
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int n_here = min(PAGE, a.n_new - tile * PAGE);
+    const int p0 = sq.len0 + tile * PAGE;
+    const uint16_t* ksrc = a.k + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
+    const uint16_t* vsrc = a.v + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
+    // page of this tile (INT2 tiles only), fetched before the tile's work
+    const int page = (n_int2 > 0 && p0 >= SINK) ? a.page_table[static_cast<size_t>(sq.seq) * a.max_pages + (tile - 1)] : 0;
+    // a 64 x 128 bf16 tile (keys, later values) into LDS, 16 bytes per thread and step; rows past
+    // the call's tokens are zero
+    auto load_tile = [&](const uint16_t* src) {
+      v4u_w w[4];
 #pragma unroll
-      for (int u = 0; u < GROUP; ++u)
-        vals[u] = isv ? bf16_to_f32(vsrc[static_cast<size_t>(j) * row + 64 * g + u]) : x[j][64 * g + u];
-      mn = vals[0];
-      mx = vals[0];
-#pragma unroll
-      for (int u = 1; u < GROUP; ++u) {
-        mn = fminf(mn, vals[u]);
-        mx = fmaxf(mx, vals[u]);
+      for (int r = 0; r < 4; ++r) {
+        const int i = tid + 256 * r, j = i >> 4, c8 = i & 15;
+        w[r] = v4u_w{0u, 0u, 0u, 0u};
+        if (j < n_here) w[r] = *reinterpret_cast<const v4u_w*>(src + static_cast<size_t>(j) * row + 8 * c8);
       }
-      const QParams q = quant_params(mn, mx, isv ? C_V : C_K);
-      uint8_t (*dst)[D] = isv ? vc : kc;
 #pragma unroll
-      for (int u = 0; u < GROUP; ++u) dst[j][64 * g + u] = (q.s16 != 0) ? static_cast<uint8_t>(quant_code(vals[u], q)) : 0;
-      meta[j][4 * isv + 2 * g] = q.s16;
-      meta[j][4 * isv + 2 * g + 1] = q.lo16;
-    } else {
-      uint8_t (*dst)[D] = isv ? vc : kc;
-      for (int u = 0; u < GROUP; ++u) dst[j][64 * g + u] = 0;
-      meta[j][4 * isv + 2 * g] = 0;
-      meta[j][4 * isv + 2 * g + 1] = 0;
+      for (int r = 0; r < 4; ++r) {
+        const int i = tid + 256 * r;
+        *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = w[r];
+      }
+    };
+    load_tile(ksrc);
+    __syncthreads();
+
+    // rotation: 16-token column tiles; each (output tile, K-step) takes the three R^T terms
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v8bf b[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const v8bf*>(&tin[16 * nt + n16][32 * ks + 8 * q4]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        v4f_w acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int t = 2; t >= 0; --t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt][ks][t], b[ks], acc, 0, 0, 0);
+        *reinterpret_cast<v4f_w*>(&x[16 * nt + n16][32 * wave + 16 * mt + 4 * q4]) = acc;
+      }
     }
+    __syncthreads();
+    load_tile(vsrc);
+    __syncthreads();
+
+    // BF16 destinations: sink / window (tiles holding such positions only)
+    const bool any_bf16 = (p0 < SINK) || (p0 + n_here > SINK + n_int2);
+    if (any_bf16) {
+      for (int i = tid; i < n_here * D; i += 256) {
+        const int j = i / D, c = i % D, p = p0 + j;
+        const bool int2 = (p >= SINK) && (p < SINK + n_int2);
+        if (int2) continue;
+        const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
+        a.ring[ring_head + static_cast<size_t>(slot) * D + c] = f32_to_bf16(x[j][c]);
+        a.ring[ring_head + static_cast<size_t>(RING + slot) * D + c] = tin[j][c];
+      }
+    }
+
+    // INT2 destination: tokens j with SINK <= p0 + j < SINK + n_int2 (tile >= 1 of an empty sequence)
+    int n_q = 0;
+    if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
+    if (n_q > 0) {  // uniform across the block
+      uint32_t* blk = reinterpret_cast<uint32_t*>(a.pool + (static_cast<size_t>(page) * a.hkv + kvh) * HEAD_BLOCK);
+      // one (token j, group g) per thread: waves 0-1 keys, waves 2-3 values.  The group's 64
+      // values are read twice from LDS (range, then codes) in 16-byte pieces; rows of
+      // consecutive lanes fall in distinct banks.
+      const int j = tid & 63, g = (tid >> 6) & 1, isv = tid >> 7;
+      float lo = 0.0f, inv = 0.0f;
+      uint32_t mword = 0u;
+      if (j < n_q) {
+        float mn = INFINITY, mx = -INFINITY;
+        if (isv) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const v4u_w w = *reinterpret_cast<const v4u_w*>(&tin[j][64 * g + 8 * i]);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v0 = __uint_as_float(ww[e] << 16), v1 = __uint_as_float(ww[e] & 0xFFFF0000u);
+              mn = fminf(mn, fminf(v0, v1));
+              mx = fmaxf(mx, fmaxf(v0, v1));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 4 * i]);
+            mn = fminf(mn, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+          }
+        }
+        const QParams qp = quant_params(mn, mx, isv ? C_V : C_K);
+        lo = qp.lo;
+        inv = qp.inv;  // 0 when the stored scale is 0: every code is then 0
+        mword = static_cast<uint32_t>(qp.s16) | (static_cast<uint32_t>(qp.lo16) << 16);
+      }
+      // slots without a token: minimum 0, reciprocal scale 0 -> code 0, metadata 0
+      blk[(META_OFF >> 2) + 4 * j + 2 * isv + g] = mword;
+      if (isv) {
+        qlo[j][g] = lo;
+        qinv[j][g] = inv;
+      } else {
+        // key words: 16 channels 64 g + 16 kq + u of token j per word
+        QParams qp;
+        qp.lo = lo;
+        qp.inv = inv;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 16 * kq + 4 * i]);
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) word |= quant_code(vv[e], qp) << kc_bit(4 * i + e);
+          }
+          blk[(KC_OFF >> 2) + kc_word(j, 64 * g + 16 * kq)] = word;
+        }
+      }
+      __syncthreads();
+      // value words (inverse of vc_word): 16 tokens of one channel per word
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int w = tid + 256 * r;
+        const int ct = 4 * (w >> 8) + (w & 3), ln = (w & 255) >> 2;
+        const int kq = ln >> 4, n = ln & 15, c = 16 * ct + n, gv = c >> 6;
+        uint32_t word = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int jj = 32 * s2 + 8 * kq + kk;
+            QParams qp;
+            qp.lo = qlo[jj][gv];
+            qp.inv = qinv[jj][gv];
+            word |= quant_code(bf16_to_f32(tin[jj][c]), qp) << vc_bit(jj);
+          }
+        blk[(VC_OFF >> 2) + w] = word;
+      }
+    }
+    __syncthreads();  // the next tile overwrites the tile buffer and the parameters
   }
-  __syncthreads();
-  const int page = a.page_table[static_cast<size_t>(sq.seq) * a.max_pages + (tile - 1)];
-  uint32_t* blk = reinterpret_cast<uint32_t*>(a.pool + (static_cast<size_t>(page) * a.hkv + kvh) * HEAD_BLOCK);
-  pack_block(blk, kc, vc, meta, tid);
 }
 
 hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_write, dim3(n_tiles, a.hkv, a.n_seqs), dim3(256), 0, s, a);
+  const int groups = (n_tiles + WRITE_TILES - 1) / WRITE_TILES;
+  hipLaunchKernelGGL(k_write, dim3(groups, a.hkv, a.n_seqs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ append (no INT2 output)
 // Writes that only reach the BF16 sink / window (every append into a non-empty sequence, and a
 // first write of at most 320 tokens).  Grid (KV heads, sequences of the chunk), 128 threads:
-// thread c owns output channel c of every token; the rotation uses the same fp32 FMA order as
-// the tile kernel above, so both paths store identical bf16 keys.
+// thread c owns output channel c of every token; fp32 VALU rotation (a single token per sequence
+// and head is too little work for the matrix cores).
 
 __global__ __launch_bounds__(128) void k_append(WriteArgs a) {
   const int kvh = blockIdx.x, sl = blockIdx.y, c = threadIdx.x;

@@ -114,7 +114,8 @@ typedef struct oscar_kv oscar_kv;
  *             lives in page page_table[seq][i / 64], slot i % 64.
  * rot         device, num_kv_heads * OSCAR_ROT_HEAD_BYTES bytes, written by
  *             oscar_kv_set_rotation: per KV head R_K fp32 [128][128] followed by
- *             three bf16 [128][128] terms whose sum is R_K to fp32 precision.
+ *             three bf16 [128][128] terms of its transpose (term t, output channel c,
+ *             input channel i) whose sum is R_K to fp32 precision.
  */
 typedef struct {
     int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads with Hq/Hkv <= 8 */
@@ -243,18 +244,27 @@ int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);
 int oscar_kv_set_decode_kernel(oscar_kv *kv, int32_t kernel);
 
 /* Kernel timing (measurement aid).  enable = 1 creates OSCAR_TIMING_PAIRS HIP event
- * pairs (timing-only: no system-scope fence on record); from then on every oscar_decode_attn call records one pair around each launch
- * of its split kernel (not the query preparation or the combine), on the call's
- * stream, until the pairs are used up (further launches go untimed).  enable = 0
- * destroys the events.  Returns OSCAR_E_ARG on a null handle, OSCAR_E_STATE for a
- * plan-only store, OSCAR_E_HIP if event creation fails (then timing stays off). */
+ * pairs per timed kernel (timing-only: no system-scope fence on record); from then
+ * on every call records one pair around each launch of its main kernel, on the
+ * call's stream, until that kernel's pairs are used up (further launches go
+ * untimed):
+ *   OSCAR_TIMED_DECODE  the split kernel of oscar_decode_attn (not the query
+ *                       preparation or the combine);
+ *   OSCAR_TIMED_WRITE   the write kernel of oscar_kv_write (not the page-table
+ *                       upload).
+ * enable = 0 destroys the events.  Returns OSCAR_E_ARG on a null handle,
+ * OSCAR_E_STATE for a plan-only store, OSCAR_E_HIP if event creation fails (then
+ * timing stays off). */
 #define OSCAR_TIMING_PAIRS 4096
-int oscar_kv_set_decode_timing(oscar_kv *kv, int32_t enable);
+#define OSCAR_TIMED_DECODE 0
+#define OSCAR_TIMED_WRITE  1
+int oscar_kv_set_timing(oscar_kv *kv, int32_t enable);
 
-/* Waits for the recorded pairs, writes the number of timed launches to *launches
- * and their summed duration in milliseconds to *total_ms, and frees the pairs for
- * reuse.  Timing must be on (else OSCAR_E_STATE). */
-int oscar_kv_read_decode_timing(oscar_kv *kv, int32_t *launches, double *total_ms);
+/* Waits for the pairs recorded for `kernel` (OSCAR_TIMED_*), writes the number of
+ * timed launches to *launches and their summed duration in milliseconds to
+ * *total_ms, and frees those pairs for reuse.  OSCAR_E_ARG for a null argument or
+ * an unknown kernel, OSCAR_E_STATE when timing is off. */
+int oscar_kv_read_timing(oscar_kv *kv, int32_t kernel, int32_t *launches, double *total_ms);
 
 const char *oscar_last_error(void);
 void oscar_kv_destroy(oscar_kv *kv);

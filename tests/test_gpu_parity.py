@@ -252,16 +252,16 @@ def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
         st.write([0, 1], parity.to_dev_bf16(ks), parity.to_dev_bf16(vs))
         # 38 INT2 pages + 320 BF16 tokens (weight 32 pages): 35 and 70 pages per split leave room
         # for the BF16 work in the last INT2 split (folded); 1, 3 and 38 give it its own work-group
-        st.set_decode_timing(True)
+        st.set_timing(True)
         for pps in (1, 3, 35, 38, 70, 0):
             st.set_decode_split(pps)
             a = st.decode([0, 1], q, SCALE).cpu().numpy()
             b = st.decode([0, 1], q, SCALE).cpu().numpy()
             assert np.array_equal(a, b), "decode is not deterministic"
             outs[(order, pps)] = a
-        n_timed, ms = st.read_decode_timing()
+        n_timed, ms = st.read_timing(gpu_lib.TIMED_DECODE)
         assert n_timed == 12 and ms > 0.0
-        st.set_decode_timing(False)
+        st.set_timing(False)
         gpu = parity.export(st)
         lens = np.array([L, L])
         iso = attention.decode(gpu[0], gpu[1], gpu[2], lens, lens - 320, rot, qb, [0, 1], SCALE, hq)

@@ -135,11 +135,15 @@ def test_workspace_bytes_and_split_choice():
     assert nb4 == 2 * 8 * 6 * 130 * 4 + qprep
 
 
-def test_decode_timing_errors():
+def test_timing_errors():
     s = _plan_store()
     with pytest.raises(oscar.OscarError) as e:
-        s.set_decode_timing(True)
+        s.set_timing(True)
     assert e.value.status == oscar.E_STATE
+    for kernel in (oscar.TIMED_DECODE, oscar.TIMED_WRITE):
+        with pytest.raises(oscar.OscarError) as e:
+            s.read_timing(kernel)
+        assert e.value.status == oscar.E_STATE
     with pytest.raises(oscar.OscarError) as e:
-        s.read_decode_timing()
-    assert e.value.status == oscar.E_STATE
+        s.read_timing(2)
+    assert e.value.status == oscar.E_ARG
