@@ -98,7 +98,7 @@ __device__ inline QParams quant_params(float mn, float mx, float c) {
 __device__ inline uint32_t quant_code(float x, const QParams& q) {
 #pragma clang fp contract(off)
   const float t = (x - q.lo) * q.inv;
-  const float r = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
+  const float r = __builtin_amdgcn_fmed3f(rintf(t), 0.0f, 3.0f);  // clamp to [0, 3]
   return static_cast<uint32_t>(r);
 }
 

@@ -139,7 +139,7 @@ __device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 // Exponent e of the f16 denormal a value code lands in, by its position p' = 4 s + kk/2
 // within the 32-bit word (see the unpack in the page loop).
 __device__ inline int vcode_exp(int p) {
-  constexpr int E[8] = {0, 2, 4, 6, 8, 4, 6, 8};
+  constexpr int E[8] = {4, 6, 4, 6, 8, 4, 6, 8};
   return E[p];
 }
 
@@ -444,8 +444,8 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       const uint32_t w = (ct < 4) ? vc0[ct & 3] : vc1[ct & 3];
-      const uint32_t hi6 = w >> 6;
-      const v8h b0 = as_h8(w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u);
+      const uint32_t lo4 = w << 4, hi6 = w >> 6;
+      const v8h b0 = as_h8(lo4 & 0x00300030u, lo4 & 0x00C000C0u, w & 0x00300030u, w & 0x00C000C0u);
       const v8h b1 = as_h8(w & 0x03000300u, hi6 & 0x00300030u, hi6 & 0x00C000C0u, hi6 & 0x03000300u);
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA0, b0, oacc[ct], 0, 0, 0);
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA1, b1, oacc[ct], 0, 0, 0);

@@ -51,11 +51,11 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 // empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.
 //
 // Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_bf16.  The
-// A operand is R^T as three bf16 terms (r0 + r1 + r2 = R to fp32 precision), the B operand the
-// bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
+// A operand is R^T as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0) (|R - r0 - r1| <= 2^-18 |R|),
+// the B operand the bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
 // its R^T operands in registers for all tiles of the work-group.
 
-constexpr int WRITE_TILES = 4;
+constexpr int WRITE_TILES = 8;
 constexpr int XS = D + 4;  // fp32 row stride of the rotated tile (16-byte aligned rows)
 constexpr int KS = D + 8;  // bf16 row stride of the key tile
 
@@ -77,18 +77,18 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
   // The tile buffer holds the bf16 keys (rotation input), then the bf16 values (quantizer input).
   __shared__ uint16_t tin[PAGE][KS];
   __shared__ float x[PAGE][XS];            // rotated keys, fp32
-  // value quantizer parameters per (token, group): fp32 minimum and reciprocal scale
-  __shared__ float qlo[PAGE][2], qinv[PAGE][2];
+  // quantizer parameters per (token, K/V group 2 isv + g): fp32 minimum and reciprocal scale
+  __shared__ float qlo[PAGE][4], qinv[PAGE][4];
 
-  // A operands: R^T rows of this wave's output channels, 4 K-steps of 32 input channels, 3 terms
+  // A operands: R^T rows of this wave's output channels, 4 K-steps of 32 input channels, 2 terms
   const uint16_t* terms = reinterpret_cast<const uint16_t*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES + D * D * 4);
-  v8bf aop[2][4][3];
+  v8bf aop[2][4][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int t = 0; t < 3; ++t)
+      for (int t = 0; t < 2; ++t)
         aop[mt][ks][t] = *reinterpret_cast<const v8bf*>(terms + t * D * D + (32 * wave + 16 * mt + n16) * D + 32 * ks + 8 * q4);
 
   const size_t row = static_cast<size_t>(a.hkv) * D;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
     load_tile(ksrc);
     __syncthreads();
 
-    // rotation: 16-token column tiles; each (output tile, K-step) takes the three R^T terms
+    // rotation: 16-token column tiles; each (output tile, K-step) takes the two R^T terms
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       v8bf b[4];
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int t = 2; t >= 0; --t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt][ks][t], b[ks], acc, 0, 0, 0);
+          for (int t = 1; t >= 0; --t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt][ks][t], b[ks], acc, 0, 0, 0);
         *reinterpret_cast<v4f_w*>(&x[16 * nt + n16][32 * wave + 16 * mt + 4 * q4]) = acc;
       }
     }
@@ -157,63 +157,66 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
     if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
     if (n_q > 0) {  // uniform across the block
       uint32_t* blk = reinterpret_cast<uint32_t*>(a.pool + (static_cast<size_t>(page) * a.hkv + kvh) * HEAD_BLOCK);
-      // one (token j, group g) per thread: waves 0-1 keys, waves 2-3 values.  The group's 64
-      // values are read twice from LDS (range, then codes) in 16-byte pieces; rows of
-      // consecutive lanes fall in distinct banks.
-      const int j = tid & 63, g = (tid >> 6) & 1, isv = tid >> 7;
-      float lo = 0.0f, inv = 0.0f;
-      uint32_t mword = 0u;
-      if (j < n_q) {
-        float mn = INFINITY, mx = -INFINITY;
-        if (isv) {
+      // ranges and parameters: one (token j, group g) per thread, waves 0-1 keys, waves 2-3 values.
+      // The group's 64 values are read in 16-byte pieces; rows of consecutive lanes fall in
+      // distinct banks.
+      {
+        const int j = tid & 63, g = (tid >> 6) & 1, isv = tid >> 7;
+        float lo = 0.0f, inv = 0.0f;
+        uint32_t mword = 0u;
+        if (j < n_q) {
+          float mn = INFINITY, mx = -INFINITY;
+          if (isv) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const v4u_w w = *reinterpret_cast<const v4u_w*>(&tin[j][64 * g + 8 * i]);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            for (int i = 0; i < 8; ++i) {
+              const v4u_w w = *reinterpret_cast<const v4u_w*>(&tin[j][64 * g + 8 * i]);
+              const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float v0 = __uint_as_float(ww[e] << 16), v1 = __uint_as_float(ww[e] & 0xFFFF0000u);
-              mn = fminf(mn, fminf(v0, v1));
-              mx = fmaxf(mx, fmaxf(v0, v1));
+              for (int e = 0; e < 4; ++e) {
+                const float v0 = __uint_as_float(ww[e] << 16), v1 = __uint_as_float(ww[e] & 0xFFFF0000u);
+                mn = fminf(mn, fminf(v0, v1));
+                mx = fmaxf(mx, fmaxf(v0, v1));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 4 * i]);
+              mn = fminf(fminf(mn, v.x), fminf(v.y, fminf(v.z, v.w)));
+              mx = fmaxf(fmaxf(mx, v.x), fmaxf(v.y, fmaxf(v.z, v.w)));
             }
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 4 * i]);
-            mn = fminf(mn, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
-            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-          }
+          const QParams qp = quant_params(mn, mx, isv ? C_V : C_K);
+          lo = qp.lo;
+          inv = qp.inv;  // 0 when the stored scale is 0: every code is then 0
+          mword = static_cast<uint32_t>(qp.s16) | (static_cast<uint32_t>(qp.lo16) << 16);
         }
-        const QParams qp = quant_params(mn, mx, isv ? C_V : C_K);
-        lo = qp.lo;
-        inv = qp.inv;  // 0 when the stored scale is 0: every code is then 0
-        mword = static_cast<uint32_t>(qp.s16) | (static_cast<uint32_t>(qp.lo16) << 16);
-      }
-      // slots without a token: minimum 0, reciprocal scale 0 -> code 0, metadata 0
-      blk[(META_OFF >> 2) + 4 * j + 2 * isv + g] = mword;
-      if (isv) {
-        qlo[j][g] = lo;
-        qinv[j][g] = inv;
-      } else {
-        // key words: 16 channels 64 g + 16 kq + u of token j per word
-        QParams qp;
-        qp.lo = lo;
-        qp.inv = inv;
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 16 * kq + 4 * i]);
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) word |= quant_code(vv[e], qp) << kc_bit(4 * i + e);
-          }
-          blk[(KC_OFF >> 2) + kc_word(j, 64 * g + 16 * kq)] = word;
-        }
+        // slots without a token: minimum 0, reciprocal scale 0 -> code 0, metadata 0
+        blk[(META_OFF >> 2) + 4 * j + 2 * isv + g] = mword;
+        qlo[j][2 * isv + g] = lo;
+        qinv[j][2 * isv + g] = inv;
       }
       __syncthreads();
+      // key words (inverse of kc_word): 16 channels 64 g + 16 kq + u of one token per word
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int w = tid + 256 * r;
+        const int t2 = w >> 8, ln = (w & 255) >> 2, d = w & 3;
+        const int t = 2 * t2 + (d >> 1), g = d & 1, kq = ln >> 4, n = ln & 15;
+        const int j = 16 * t + n;
+        QParams qp;
+        qp.lo = qlo[j][g];
+        qp.inv = qinv[j][g];
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4f_w v = *reinterpret_cast<const v4f_w*>(&x[j][64 * g + 16 * kq + 4 * i]);
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) word |= quant_code(vv[e], qp) << kc_bit(4 * i + e);
+        }
+        blk[(KC_OFF >> 2) + w] = word;
+      }
       // value words (inverse of vc_word): 16 tokens of one channel per word
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
           for (int kk = 0; kk < 8; ++kk) {
             const int jj = 32 * s2 + 8 * kq + kk;
             QParams qp;
-            qp.lo = qlo[jj][gv];
-            qp.inv = qinv[jj][gv];
+            qp.lo = qlo[jj][2 + gv];
+            qp.inv = qinv[jj][2 + gv];
             word |= quant_code(bf16_to_f32(tin[jj][c]), qp) << vc_bit(jj);
           }
         blk[(VC_OFF >> 2) + w] = word;

@@ -53,14 +53,17 @@ def _kv_batch(cfg, seqs, hkv, n, token0=0):
 
 
 def _ring_key_bound(k_bits, rot_h):
-    """Allowed |stored bf16 key - exact k.R| per channel: half a bf16 ulp of the stored value plus the
-    fp32 dot-product forward-error bound gamma_128 * sum_i |k_i R_ij| (Higham, Accuracy and Stability
-    of Numerical Algorithms, section 3.1)."""
+    """Allowed |stored bf16 key - exact k.R| per channel, besides half a bf16 ulp of the stored value.
+    Multi-token writes rotate on the matrix cores with R split into bf16 terms r0 + r1 (each the
+    bf16 rounding of the remainder, so |R - r0 - r1| <= 2^-18 |R|) and fp32 accumulation of the
+    256 products k_i r0_ij, k_i r1_ij; single-token appends use a 128-term fp32 dot product.  Both
+    stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-18 sum_i |k_i R_ij| (dot-product
+    forward-error bound, Higham, Accuracy and Stability of Numerical Algorithms, section 3.1)."""
     k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
     r = np.asarray(rot_h, np.float32).astype(np.float64)
     u = 2.0 ** -24
-    gamma = 128 * u / (1 - 128 * u)
-    return np.abs(k) @ np.abs(r) * gamma, k @ r
+    gamma = 256 * u / (1 - 256 * u)
+    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -18), k @ r
 
 
 def _bf16_ulp(x):
