@@ -24,6 +24,7 @@ constexpr int PAGE = 64;
 constexpr int SINK = 64;
 constexpr int WIN = 256;
 constexpr int RING = 320;
+static_assert(RING == 64 * RING_CHUNKS, "the ring is five 64-slot chunks");
 constexpr int HEAD_BLOCK = 5120;
 constexpr int KC_OFF = 0;
 constexpr int VC_OFF = 2048;

@@ -187,8 +187,7 @@ __global__ __launch_bounds__(256) void k_decode_simple(DecodeArgs a) {
 __global__ __launch_bounds__(128) void k_combine(DecodeArgs a) {
   const int h = blockIdx.x, sl = blockIdx.y, c = threadIdx.x;
   const DecodeSeq sq = a.seqs[sl];
-  const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
-  const int n_split = (n_pages + a.pages_per_split - 1) / a.pages_per_split + 1;
+  const int n_split = unit_records(sq.n_int2, sq.len, a.pages_per_split, a.kernel);
   const float* rec0 = a.part + (static_cast<size_t>(sl) * a.hq + h) * a.n_split_max * PART_STRIDE;
   __shared__ float wsh[128];
   __shared__ float red[2];

@@ -144,14 +144,15 @@ __device__ inline int vcode_exp(int p) {
 }
 
 // ------------------------------------------------------------------ BF16 sink + window split
-// One wavefront over the ring in five 64-slot chunks.  Scores: lane = ring slot, the lane reads
+// One wavefront over 64-slot chunks [ch0, ch1) of the ring (a range without any token writes the
+// empty record m = -inf, l = 0, o = 0).  Scores: lane = ring slot, the lane reads
 // its own key row (all sixteen 16-byte pieces in flight at once).  Value product: lane = channel
 // pair, token rows read in batches of 16 so that 16 loads are in flight.  Slots that hold no
 // token are masked by a wave-uniform ballot; their (possibly uninitialised) rows never reach
 // the sums.
 template <int G>
-__device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, const float* qf,
-                           float (*pbuf)[64]) {
+__device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, int ch0, int ch1,
+                           const float* qf, float (*pbuf)[64]) {
   constexpr int KB = (G == 8) ? 4 : 8;    // key pieces in flight per lane
   constexpr int VB = 8;                  // value rows in flight
   const int lane = threadIdx.x;
@@ -164,7 +165,7 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
   float m[G], l[G], o0[G], o1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.0f; o0[h] = 0.0f; o1[h] = 0.0f; }
-  for (int ch = 0; ch < RING / 64; ++ch) {
+  for (int ch = ch0; ch < ch1; ++ch) {
     const int slot = ch * 64 + lane;
     const bool ok = (slot < SINK) ? (slot < n_sink) : (((slot - SINK - wfirst + WIN) % WIN) < n_win);
     const uint64_t okmask = __ballot(ok);
@@ -248,10 +249,11 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   const DecodeSeq sq = a.seqs[sl];
   const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
   const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
-  // the BF16 sink + window tokens (partial record n_isplits) ride on the last INT2 split when
-  // it has room for them, else they are work-group n_isplits
+  const int n_bsplits = bf16_splits(sq.n_int2, sq.len, a.pages_per_split, 0);
+  // the BF16 sink + window tokens (partial records n_isplits ..) ride on the last INT2 split
+  // when it has room for them, else they are work-groups n_isplits .. n_isplits + n_bsplits - 1
   const bool fold = bf16_folded(sq.n_int2, sq.len, a.pages_per_split, 0);
-  if (split >= n_isplits + (fold ? 0 : 1)) return;
+  if (split >= n_isplits + (fold ? 0 : n_bsplits)) return;
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
                       (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
@@ -259,8 +261,10 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   // P operand staging: hi rows (group, head) then lo rows; GQA <= 4: hi 0..7, lo 8..15,
   // GQA 8: hi 0..15, lo 16..31
   __shared__ _Float16 plds[32][64];
-  if (split == n_isplits) {
-    bf16_split<G>(a, sq, kvh, sl, n_isplits, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+  if (split >= n_isplits) {
+    const int b = split - n_isplits;
+    bf16_split<G>(a, sq, kvh, sl, split, (RING_CHUNKS * b) / n_bsplits, (RING_CHUNKS * (b + 1)) / n_bsplits,
+                  reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
     return;
   }
 
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     }
   }
   if (fold && split == n_isplits - 1)
-    bf16_split<G>(a, sq, kvh, sl, n_isplits, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+    bf16_split<G>(a, sq, kvh, sl, n_isplits, 0, RING_CHUNKS, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
 }
 
 // Work-groups to plan for one residency round: all wave slots of the device but one per

@@ -75,27 +75,41 @@ struct DecodeArgs {
   int32_t hkv, hq, max_pages, n_seqs;
   int32_t pages_per_split, n_split_max;
   float scale_log2;       // sm_scale * log2(e)
-  int32_t pad;
+  int32_t kernel;         // 0 matrix-core split kernel, 1 reference kernel (record layout)
   DecodeSeq seqs[CHUNK];
 };
 
 constexpr int PART_STRIDE = 130;
 
 // Work split of one (sequence, KV head) unit.  INT2 split s covers pages
-// [s pps, min((s+1) pps, n_pages)) and writes partial record s; the BF16 sink + window
-// tokens write record ceil(n_pages / pps).  A BF16 token moves 512 bytes (key and value
-// rows), an INT2 page 5120, so ten BF16 tokens weigh one page.  On the matrix-core path
-// the last INT2 split also does the BF16 work when its spare capacity holds that weight;
-// otherwise the BF16 work is a work-group of its own.
+// [s pps, min((s+1) pps, n_pages)) and writes partial record s.  The BF16 sink + window tokens
+// (five 64-slot chunks of the ring) follow as records n_is .. n_is + nb - 1, where n_is is the
+// number of INT2 splits: a BF16 token moves 512 bytes (key and value rows), an INT2 page 5120,
+// so ten BF16 tokens weigh one page, and the BF16 work is cut into nb = ceil(weight / pps)
+// (1..5) work-groups of whole chunks so that none of them outweighs an INT2 split.  On the
+// matrix-core path (kernel 0) a single BF16 work-group rides on the last INT2 split when that
+// split's spare capacity holds its weight.  The reference kernel (kernel 1) keeps one BF16
+// work-group.
+constexpr int RING_CHUNKS = 5;
 __host__ __device__ inline int bf16_page_weight(int n_bf16) { return (n_bf16 + 9) / 10; }
 __host__ __device__ inline int int2_splits(int n_int2, int pps) { return ((n_int2 + 63) / 64 + pps - 1) / pps; }
+__host__ __device__ inline int bf16_splits(int n_int2, int len, int pps, int kernel) {
+  if (kernel != 0) return 1;
+  const int nb = (bf16_page_weight(len - n_int2) + pps - 1) / pps;
+  return nb < 1 ? 1 : (nb > RING_CHUNKS ? RING_CHUNKS : nb);
+}
 __host__ __device__ inline bool bf16_folded(int n_int2, int len, int pps, int kernel) {
   const int n_pages = (n_int2 + 63) / 64, n_is = (n_pages + pps - 1) / pps;
-  return kernel == 0 && n_is > 0 && n_is * pps - n_pages >= bf16_page_weight(len - n_int2);
+  return kernel == 0 && n_is > 0 && bf16_splits(n_int2, len, pps, kernel) == 1 &&
+         n_is * pps - n_pages >= bf16_page_weight(len - n_int2);
+}
+// partial records of one unit (the combine's count; the workspace holds the maximum per call)
+__host__ __device__ inline int unit_records(int n_int2, int len, int pps, int kernel) {
+  return int2_splits(n_int2, pps) + bf16_splits(n_int2, len, pps, kernel);
 }
 // work-groups of the split kernel for one unit
 __host__ __device__ inline int unit_workgroups(int n_int2, int len, int pps, int kernel) {
-  return int2_splits(n_int2, pps) + (bf16_folded(n_int2, len, pps, kernel) ? 0 : 1);
+  return int2_splits(n_int2, pps) + (bf16_folded(n_int2, len, pps, kernel) ? 0 : bf16_splits(n_int2, len, pps, kernel));
 }
 
 hipError_t launch_fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s);

@@ -429,8 +429,11 @@ int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int
   if (rc) return rc;
   const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
   int64_t max_split = 1;
-  for (int i = 0; i < n_seqs; ++i)
-    max_split = std::max(max_split, ceil_div(ceil_div(kv->n_int2[seq_ids[i]], kPage), pps) + 1);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]),
+                                                          static_cast<int>(pps), kv->decode_kernel));
+  }
   const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
   *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float) +
            static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE;
@@ -475,9 +478,11 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     for (int i = 0; i < a.n_seqs; ++i) {
       const int s = seq_ids[c0 + i];
       a.seqs[i] = DecodeSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), c0 + i};
-      max_split = std::max(max_split, ceil_div(ceil_div(kv->n_int2[s], kPage), pps) + 1);
+      max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]),
+                                                            static_cast<int>(pps), kv->decode_kernel));
     }
     a.n_split_max = static_cast<int32_t>(max_split);
+    a.kernel = kv->decode_kernel;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
     hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st, t0, t1) : launch_decode_mfma(a, st, t0, t1);

@@ -131,8 +131,17 @@ def test_workspace_bytes_and_split_choice():
     assert nb > qprep and (nb - qprep) % (130 * 4) == 0
     s.set_decode_split(4)
     nb4 = s.workspace_bytes([0, 1])
-    # 20 pages / 4 per split = 5 INT2 splits + 1 BF16 split, 2 seqs x 8 q heads, 130 floats each
-    assert nb4 == 2 * 8 * 6 * 130 * 4 + qprep
+    # sequence 0: 20 pages / 4 per split = 5 INT2 records; its 320 BF16 tokens weigh 32 pages,
+    # cut into min(5, ceil(32 / 4)) = 5 chunk ranges -> 10 records.  Sequence 1 (100 tokens, no
+    # INT2): weight 10 -> ceil(10 / 4) = 3 records.  2 seqs x 8 q heads x 10 records x 130 floats
+    assert nb4 == 2 * 8 * 10 * 130 * 4 + qprep
+    s.set_decode_split(40)
+    # 1 INT2 record + 1 BF16 record (weight 32 <= 40 pages per split)
+    assert s.workspace_bytes([0, 1]) == 2 * 8 * 2 * 130 * 4 + qprep
+    s.set_decode_kernel(1)
+    s.set_decode_split(4)
+    # the reference kernel keeps one BF16 record per unit: 5 + 1
+    assert s.workspace_bytes([0, 1]) == 2 * 8 * 6 * 130 * 4 + qprep
 
 
 def test_timing_errors():
