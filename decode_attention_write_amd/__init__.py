@@ -34,7 +34,7 @@ _NAMES = {E_ARG: "E_ARG", E_NOPAGE: "E_NOPAGE", E_WINDOW_FULL: "E_WINDOW_FULL", 
           E_NUMERIC: "E_NUMERIC", E_HIP: "E_HIP", E_WORKSPACE: "E_WORKSPACE", E_STATE: "E_STATE"}
 
 EXPORTS = [
-    "oscar_calibrate_host", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
+    "oscar_calibrate_host", "oscar_calibrate_value_host", "oscar_fold_value_rotation", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
     "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_timing",
@@ -70,6 +70,8 @@ def load():
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
         "oscar_calibrate_host": [P, I64, I32, P, P],
+        "oscar_calibrate_value_host": [P, P, I64, I64, I32, P, P],
+        "oscar_fold_value_rotation": [I32, I32, I32, P, P, P],
         "oscar_kv_buffer_bytes": [P, P, P, P, P],
         "oscar_kv_create": [P, P, I32, P, P],
         "oscar_kv_set_rotation": [P, P, P],
@@ -129,6 +131,34 @@ def oscar_calibrate_host(q_rows):
     _check(load().oscar_calibrate_host(q.ctypes.data_as(ctypes.c_void_p), q.shape[0], q.shape[1],
                                        rot.ctypes.data_as(ctypes.c_void_p), eig.ctypes.data_as(ctypes.c_void_p)))
     return rot, eig
+
+
+def oscar_calibrate_value_host(s_probs, v_rows):
+    """R_V (float32 [128,128]) and descending eigenvalues of C_S from calibration attention
+    probabilities s [n_q, n_tok] and values v [n_tok, 128] (host)."""
+    s = np.ascontiguousarray(np.asarray(s_probs, dtype=np.float32))
+    v = np.ascontiguousarray(np.asarray(v_rows, dtype=np.float32))
+    if s.ndim != 2 or v.ndim != 2 or s.shape[1] != v.shape[0]:
+        raise ValueError("s must be [n_q, n_tok] and v [n_tok, 128]")
+    rot = np.empty((HEAD_DIM, HEAD_DIM), dtype=np.float32)
+    eig = np.empty(HEAD_DIM, dtype=np.float64)
+    _check(load().oscar_calibrate_value_host(s.ctypes.data_as(ctypes.c_void_p), v.ctypes.data_as(ctypes.c_void_p),
+                                             s.shape[0], s.shape[1], v.shape[1],
+                                             rot.ctypes.data_as(ctypes.c_void_p), eig.ctypes.data_as(ctypes.c_void_p)))
+    return rot, eig
+
+
+def oscar_fold_value_rotation(w_v, w_o, r_v, num_q_heads, num_kv_heads):
+    """Fold R_V into copies of w_v [d_model, Hkv*128] and w_o [Hq*128, d_model] (host, float32)."""
+    wv = np.array(w_v, dtype=np.float32, order="C", copy=True)
+    wo = np.array(w_o, dtype=np.float32, order="C", copy=True)
+    r = np.ascontiguousarray(np.asarray(r_v, dtype=np.float32))
+    if wv.shape[1] != num_kv_heads * HEAD_DIM or wo.shape != (num_q_heads * HEAD_DIM, wv.shape[0]) \
+            or r.shape != (num_kv_heads, HEAD_DIM, HEAD_DIM):
+        raise ValueError("shape mismatch between w_v, w_o, r_v and the head counts")
+    _check(load().oscar_fold_value_rotation(wv.shape[0], num_q_heads, num_kv_heads, r.ctypes.data_as(ctypes.c_void_p),
+                                            wv.ctypes.data_as(ctypes.c_void_p), wo.ctypes.data_as(ctypes.c_void_p)))
+    return wv, wo
 
 
 def oscar_kv_write(store, seq_ids, k, v, stream=None):

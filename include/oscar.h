@@ -148,6 +148,42 @@ typedef struct {
  */
 int oscar_calibrate_host(const float *q, int64_t n, int32_t d, float *rot_out, double *eig_out);
 
+/*
+ * Offline value-rotation calibration ([A] rotation section: R_V = U_S . H_Had .
+ * P_br with U_S the eigenvectors of C_S = (1/N) V^T S^T S V), on the host in fp64.
+ *
+ * s        host fp32 [n_q][n_tok]: attention probabilities of n_q calibration
+ *          queries over n_tok calibration tokens (rows normally sum to 1; pool
+ *          the queries of every q head that reads this KV head).
+ * v        host fp32 [n_tok][d]: the (unrotated) values of those tokens.
+ * d        must be 128.
+ * rot_out  host fp32 [d][d], row-major R_V (values are stored as v . R_V).
+ * eig_out  host fp64 [d] eigenvalues of C_S, descending; may be NULL.
+ * C_S is accumulated as the second moment of the attention outputs o_n = s_n V.
+ * Eigenvector order and signs, H and P_br as for oscar_calibrate_host.
+ * Errors: OSCAR_E_ARG (null, sizes), OSCAR_E_NUMERIC (non-finite input,
+ * eigensolver failure).
+ */
+int oscar_calibrate_value_host(const float *s, const float *v, int64_t n_q, int64_t n_tok, int32_t d,
+                               float *rot_out, double *eig_out);
+
+/*
+ * Absorb R_V into a layer's projections, in place, on the host ([A] rotation
+ * section: R_V is folded offline into the value/output projections, so the cache
+ * stores rotated values at no runtime cost and oscar_decode_attn's output, which
+ * is in the R_V basis, is un-rotated by the output projection).
+ *
+ * w_v  host fp32 [d_model][num_kv_heads * 128] row-major (x . w_v = values);
+ *      columns of KV head h become w_v[:, h block] . R_V[h].
+ * w_o  host fp32 [num_q_heads * 128][d_model] row-major (o . w_o = output);
+ *      rows of q head j become R_V[h]^T . w_o[j block], h = j / (Hq / Hkv).
+ * r_v  host fp32 [num_kv_heads][128][128].
+ * Products are accumulated in fp64 and rounded to fp32.
+ * Errors: OSCAR_E_ARG (null, head counts), OSCAR_E_NUMERIC (non-finite r_v).
+ */
+int oscar_fold_value_rotation(int32_t d_model, int32_t num_q_heads, int32_t num_kv_heads, const float *r_v,
+                              float *w_v, float *w_o);
+
 /* Bytes the caller must allocate for each device buffer of a store with this
  * descriptor (device pointers in desc are ignored).  Any output may be NULL. */
 int oscar_kv_buffer_bytes(const oscar_kv_desc *desc, size_t *pool, size_t *ring,

@@ -1,4 +1,4 @@
-"""Key-rotation calibration, fp64.  Test infrastructure only (see package header).
+"""Key- and value-rotation calibration, fp64.  Test infrastructure only (see package header).
 
 Follows axbrief, section "어텐션 통계 기반 회전과 Triton 커널의 결합" (attention-
 statistics rotation): the key rotation is built from the eigenvectors U_Q of the
@@ -17,7 +17,10 @@ Readings taken where the pages are silent:
 * a key row k is rotated as k' = k . R_K; a query row likewise, q' = q . R_K.
 
 Parity: pinned (orthogonality, closed-form H and P_br, exact-covariance
-eigen input, statistical spectrum, attention equivalence).
+eigen input, statistical spectrum, attention equivalence; value side: the
+printed C_S against the second moment of the attention outputs, a closed-form
+eigenbasis, exact output equivalence of rotated values and the folded output
+projection).
 """
 from __future__ import annotations
 
@@ -82,3 +85,50 @@ def key_rotation(q_rows):
     w, u = eig_descending(c)
     d = c.shape[0]
     return u @ sylvester_hadamard(d) @ bit_reversal_matrix(d), w
+
+
+# ---------------------------------------------------------------- value side
+# Same page and section: the value rotation is R_V = U_S . H_Had . P_br with U_S
+# the eigenvectors of C_S = (1/N) V^T S^T S V, where S holds the calibration
+# queries' attention probabilities over the calibration tokens and V their
+# values; R_V is absorbed offline into the value and output projections, so the
+# cache stores values already rotated and attention outputs come out in the
+# R_V basis.
+#
+# Readings: S is [N queries, T tokens] (rows sum to 1), V is [T, d]; (S V) holds
+# the N attention outputs as rows, so C_S is their second moment (no mean
+# subtracted); GQA: the queries of every head that reads the KV head are pooled
+# (as for C_Q); ordering, signs, H and P_br as for R_K.
+
+def value_moment(s, v) -> np.ndarray:
+    """C_S = (1/N) V^T S^T S V, evaluated as printed (fp64)."""
+    s = np.asarray(s, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    return v.T @ s.T @ s @ v / s.shape[0]
+
+
+def value_rotation(s, v):
+    """R_V = U_S . H . P_br (fp64) and the eigenvalues of C_S (descending)."""
+    c = value_moment(s, v)
+    w, u = eig_descending(c)
+    d = c.shape[0]
+    return u @ sylvester_hadamard(d) @ bit_reversal_matrix(d), w
+
+
+def fold_value_rotation(w_v, w_o, r_v, hq: int, hkv: int):
+    """Absorb R_V into the projections (fp64): for KV head h the value-projection
+    columns h*d .. h*d+d-1 become W_V[:, block] . R_V[h] (values come out rotated),
+    and for every query head j reading KV head h = j // (hq/hkv) the output-
+    projection rows j*d .. j*d+d-1 become R_V[h]^T . W_O[block] (undoing the
+    rotation of that head's attention output)."""
+    w_v = np.array(w_v, dtype=np.float64)
+    w_o = np.array(w_o, dtype=np.float64)
+    r_v = np.asarray(r_v, dtype=np.float64)
+    d = r_v.shape[-1]
+    g = hq // hkv
+    for h in range(hkv):
+        w_v[:, h * d:(h + 1) * d] = w_v[:, h * d:(h + 1) * d] @ r_v[h]
+    for j in range(hq):
+        h = j // g
+        w_o[j * d:(j + 1) * d, :] = r_v[h].T @ w_o[j * d:(j + 1) * d, :]
+    return w_v, w_o

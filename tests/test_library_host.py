@@ -156,3 +156,49 @@ def test_timing_errors():
     with pytest.raises(oscar.OscarError) as e:
         s.read_timing(2)
     assert e.value.status == oscar.E_ARG
+
+
+def test_calibrate_value_host_matches_oracle():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((512, 128))           # more queries than channels: full-rank C_S
+    k = rng.standard_normal((400, 128))
+    s = np.exp((q @ k.T) / np.sqrt(128) * 4)
+    s /= s.sum(axis=1, keepdims=True)
+    v = rng.standard_normal((400, 128)) * (1 + np.arange(128) / 16) + rng.standard_normal(128)
+    s32, v32 = s.astype(np.float32), v.astype(np.float32)
+    rot, eig = oscar.oscar_calibrate_value_host(s32, v32)
+    r_ref, w_ref = calibration.value_rotation(s32.astype(np.float64), v32.astype(np.float64))
+    assert np.abs(eig - w_ref).max() < 1e-12 * w_ref[0]
+    # eigenvectors of close eigenvalues are determined to ~eps*|C|/gap; compare per column
+    hp = calibration.bit_reversal_matrix(128).T @ calibration.sylvester_hadamard(128)
+    u, u_ref = rot.astype(np.float64) @ hp, r_ref @ hp
+    gaps = np.minimum(np.abs(np.diff(w_ref, prepend=np.inf)), np.abs(np.diff(w_ref, append=-np.inf)))
+    col_err = np.abs(u - u_ref).max(axis=0)
+    assert np.all(col_err <= 2e-7 + 1e-14 * w_ref[0] / gaps * 100), col_err.max()
+    r64 = rot.astype(np.float64)
+    assert np.abs(r64.T @ r64 - np.eye(128)).max() < 2e-6
+
+
+def test_fold_value_rotation_matches_oracle():
+    rng = np.random.default_rng(22)
+    hq, hkv, d_model = 8, 2, 64
+    r_v = np.stack([np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(hkv)]).astype(np.float32)
+    w_v = rng.standard_normal((d_model, hkv * 128)).astype(np.float32)
+    w_o = rng.standard_normal((hq * 128, d_model)).astype(np.float32)
+    wv2, wo2 = oscar.oscar_fold_value_rotation(w_v, w_o, r_v, hq, hkv)
+    wv_ref, wo_ref = calibration.fold_value_rotation(w_v, w_o, r_v, hq, hkv)
+    assert np.abs(wv2 - wv_ref).max() < 1e-5 * np.abs(wv_ref).max()
+    assert np.abs(wo2 - wo_ref).max() < 1e-5 * np.abs(wo_ref).max()
+
+
+def test_value_calibration_errors():
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_calibrate_value_host(np.full((2, 3), np.nan, np.float32), np.ones((3, 128), np.float32))
+    assert e.value.status == oscar.E_NUMERIC
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_calibrate_value_host(np.ones((2, 3), np.float32), np.ones((3, 64), np.float32))
+    assert e.value.status == oscar.E_ARG
+    bad = np.full((1, 128, 128), np.inf, np.float32)
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_fold_value_rotation(np.ones((4, 128), np.float32), np.ones((128, 4), np.float32), bad, 1, 1)
+    assert e.value.status == oscar.E_NUMERIC

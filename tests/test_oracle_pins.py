@@ -414,3 +414,70 @@ def test_decode_gqa_mapping_uniform_scores():
     vm = synth.bf16_bits_to_f32(vb[0]).astype(np.float64).mean(axis=0)    # [2, D]
     for h in range(8):
         assert np.abs(out[0, h] - vm[h // 4]).max() < 1e-6
+
+
+# ----------------------------------------------------------------------------- value rotation
+def _softmax_rows(z):
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def test_value_moment_is_second_moment_of_attention_outputs():
+    """The printed C_S = (1/N) V^T S^T S V equals the second moment of the calibration attention
+    outputs computed one query at a time by the attention routine."""
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((40, D))
+    k = rng.standard_normal((300, D))
+    v = rng.standard_normal((300, D)) + rng.standard_normal(D)
+    scale = 1 / np.sqrt(D)
+    s = _softmax_rows(scale * q @ k.T)
+    outs = np.stack([attention.attend(qi, k, v, scale)[0] for qi in q])
+    c_ref = sum(np.outer(o, o) for o in outs) / len(outs)
+    assert np.abs(calibration.value_moment(s, v) - c_ref).max() < 1e-12 * np.abs(c_ref).max()
+
+
+def test_value_rotation_closed_form_eigenbasis():
+    """S = identity and values whose rows are sqrt(128 lam_i) b_i^T: C_S = B diag(lam) B^T, so
+    U_S is B (up to the sign rule) and R_V = B . H . P_br."""
+    basis = synth.haar(D, synth.stream(98, 0, 0, 0))
+    lam = (D - np.arange(D)) / D          # distinct, well separated: eigenvectors well conditioned
+    v = np.sqrt(D * lam)[:, None] * basis.T
+    r, w = calibration.value_rotation(np.eye(D), v)
+    assert np.abs(w - lam).max() < 1e-12
+    sgn = np.sign(basis[np.argmax(np.abs(basis), axis=0), np.arange(D)])
+    expect = (basis * sgn[None, :]) @ calibration.sylvester_hadamard(D) @ calibration.bit_reversal_matrix(D)
+    assert np.abs(r - expect).max() < 1e-8
+    assert np.abs(r.T @ r - np.eye(D)).max() < 1e-12
+
+
+def test_value_rotation_and_fold_are_output_exact():
+    """Values stored as v . R_V give attention outputs o . R_V; the folded output projection
+    R_V^T . W_O turns them back into the original layer output (fp64)."""
+    rng = np.random.default_rng(12)
+    hq, hkv, d_model = 4, 2, 96
+    g = hq // hkv
+    r_v = []
+    for h in range(hkv):
+        s = _softmax_rows(rng.standard_normal((50, 200)) * 3)
+        r, _ = calibration.value_rotation(s, rng.standard_normal((200, D)) * (1 + np.arange(D) / 16))
+        r_v.append(r)
+    r_v = np.stack(r_v)
+    w_v = rng.standard_normal((d_model, hkv * D))
+    w_o = rng.standard_normal((hq * D, d_model))
+    w_v2, w_o2 = calibration.fold_value_rotation(w_v, w_o, r_v, hq, hkv)
+    x = rng.standard_normal((300, d_model))          # token activations
+    k = rng.standard_normal((hkv, 300, D))
+    q = rng.standard_normal((hq, D))
+    ref = np.zeros(d_model)
+    got = np.zeros(d_model)
+    for j in range(hq):
+        h = j // g
+        v = x @ w_v[:, h * D:(h + 1) * D]
+        v2 = x @ w_v2[:, h * D:(h + 1) * D]
+        assert np.abs(v2 - v @ r_v[h]).max() < 1e-11 * np.abs(v).max()
+        o, _, _ = attention.attend(q[j], k[h], v, 1 / np.sqrt(D))
+        o2, _, _ = attention.attend(q[j], k[h], v2, 1 / np.sqrt(D))
+        ref += o @ w_o[j * D:(j + 1) * D]
+        got += o2 @ w_o2[j * D:(j + 1) * D]
+    assert np.abs(got - ref).max() < 1e-10 * np.abs(ref).max()
