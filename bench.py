@@ -196,7 +196,7 @@ def prefill_leg(reps=5):
     kernel_us = k_ms * 1e3 / n
     nbytes = prefill_bytes(L, hkv)
     # algorithmic matrix-core work: k . R_K per token-head (2 * 128 * 128 flop); the kernel runs
-    # it three times (bf16 terms r0 + r1 + r2 of R_K)
+    # it twice (bf16 terms r0 + r1 of R_K)
     flop = 2 * 128 * 128 * L * hkv
     # appends: evict the oldest window token into INT2, then write one token, per step
     torch.cuda.synchronize()
@@ -220,7 +220,7 @@ def prefill_leg(reps=5):
         "gbps_call": round(nbytes / (float(np.median(call_ms)) * 1e3) / 1e3, 1),
         "pct_peak_kernel": round(100 * nbytes / kernel_us / 1e3 / PEAK_GBPS, 2),
         "rotation_tflops_algorithmic": round(flop / kernel_us / 1e6, 1),
-        "rotation_mfma_frac_executed": round(3 * flop / kernel_us / 1e6 / 2500.0, 4),
+        "rotation_mfma_frac_executed": round(2 * flop / kernel_us / 1e6 / 2500.0, 4),
         "append_step_us": round(append_us, 2),
     }
     log(f"prefill: call {res['call_us']} us, write kernel {res['kernel_us']} us = {res['gbps_kernel']} GB/s "
@@ -233,8 +233,8 @@ def prefill_leg(reps=5):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=36, help="development only: fewer layers")
     ap.add_argument("--context", type=int, default=100000, help="development only")
     ap.add_argument("--batch", type=int, default=32, help="development only")
@@ -266,7 +266,7 @@ def main():
     cfg = synth.CFG_QWEN3_8B
     n_layers, B, ctx = args.layers, args.batch, args.context
     hq, hkv = 32, 8
-    n_steps_total = args.warmup + args.steps
+    n_steps_total = args.warmup + 2 * args.steps  # warmup, the timed steps, the kernel-timed steps
     max_pages = -(-(ctx + n_steps_total + 64) // 64)
     num_pages = B * max_pages
     full = (n_layers, B, ctx) == (36, 32, 100000)
@@ -349,20 +349,54 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
     bytes_per_step = []
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record()
+    step_ev[0].record()
     for i in range(args.steps):
         bytes_per_step.append(step_bytes())
         step(args.warmup + i)
-    ev1.record()
+        step_ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = step_ev[0].elapsed_time(step_ev[-1])
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)])
     ms_per_step = gpu_ms / args.steps
     step_gbps = sum(bytes_per_step) / (gpu_ms / 1e3) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms/step), {step_gbps:.0f} GB/s")
+
+    # ---- the same decode steps again, with the library's fence-free HIP events around every
+    # split-kernel launch (on the launch stream): the roofline's kernel durations
+    info0 = [[st.seq_info(s) for s in seqs] for st in stores]
+    for st in stores:
+        st.set_timing(True)
+    kt0, kt1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    kt0.record()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    kt1.record()
+    torch.cuda.synchronize()
+    ms_per_step_kt = kt0.elapsed_time(kt1) / args.steps
+    k_launches, k_ms, k_each = 0, 0.0, []
+    for st in stores:
+        n, ms, each = st.read_timing(oscar.TIMED_DECODE, each=True)
+        k_launches += n
+        k_ms += ms
+        k_each.append(each)
+        st.set_timing(False)
+    k_each = np.concatenate(k_each) * 1e3  # us
+    n_chunks = -(-B // 64)
+    assert k_launches == args.steps * n_layers * n_chunks, k_launches
+    # bytes of each timed launch: step i attends over the state after its evict + append
+    kbytes_steps = [split_kernel_bytes([L + i + 1 for L, _ in info], [n2 + i + 1 for _, n2 in info], hkv)
+                    for info in info0 for i in range(args.steps)]
+    kernel_us = k_ms * 1e3 / k_launches
+    kernel_bytes = float(np.mean(kbytes_steps)) / n_chunks
+    kernel_gbps = kernel_bytes / (kernel_us / 1e6) / 1e9
+    log(f"split kernel over {args.steps} timed steps: {kernel_us:.1f} us/launch (median {np.median(k_each):.1f}), "
+        f"{kernel_gbps:.0f} GB/s ({100 * kernel_gbps / PEAK_GBPS:.1f}% of 8 TB/s); "
+        f"those steps took {ms_per_step_kt:.2f} ms each")
 
     # ---- development sweep of the split size (attention only)
     for pps in [int(x) for x in args.sweep_pps.split(",") if x]:
@@ -391,12 +425,6 @@ def main():
     for st in stores:
         info = [st.seq_info(s) for s in seqs]
         attn_bytes.append(decode_bytes([L for L, _ in info], [n2 for _, n2 in info], hq, hkv))
-    kbytes = []
-    for st in stores:
-        info = [st.seq_info(s) for s in seqs]
-        kbytes.append(split_kernel_bytes([L for L, _ in info], [n2 for _, n2 in info], hkv))
-    for st in stores:
-        st.set_timing(True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
     for r in range(args.attn_reps):
         for l, st in enumerate(stores):
@@ -405,18 +433,6 @@ def main():
             evs[l][1].record()
         torch.cuda.synchronize()
         per_call.extend(a.elapsed_time(b) for a, b in evs)
-    k_launches, k_ms = 0, 0.0
-    for st in stores:
-        n, ms = st.read_timing(oscar.TIMED_DECODE)
-        k_launches += n
-        k_ms += ms
-        st.set_timing(False)
-    n_chunks = -(-B // 64)
-    assert k_launches == args.attn_reps * n_layers * n_chunks, k_launches
-    kernel_us = k_ms * 1e3 / k_launches
-    kernel_bytes = float(np.mean(kbytes)) / n_chunks
-    kernel_gbps = kernel_bytes / (kernel_us / 1e6) / 1e9
-    log(f"split kernel: {kernel_us:.1f} us/launch, {kernel_gbps:.0f} GB/s ({100 * kernel_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
     attn_ms = float(np.mean(per_call))
     attn_gbps = float(np.mean(attn_bytes)) / (attn_ms / 1e3) / 1e9
     log(f"attention-only: {attn_ms * 1e3:.1f} us/layer, {attn_gbps:.0f} GB/s ({100 * attn_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
@@ -453,10 +469,18 @@ def main():
             "unit": "GB/s",
             "frac": round(kernel_gbps / PEAK_GBPS, 4),
             "traffic": measured_traffic() if full else None,
-            "kernel": f"k_decode_mfma<{hq // hkv}> (split-K decode attention over the INT2 pages and BF16 ring)",
+            "kernel": f"k_decode_mfma<{hq // hkv}> (split-K decode attention over the INT2 pages and BF16 ring), "
+                      f"{args.steps} timed decode steps x {n_layers} layers",
             "us_per_launch": round(kernel_us, 2),
+            "us_median": round(float(np.median(k_each)), 2),
+            "us_p10": round(float(np.percentile(k_each, 10)), 2),
+            "us_p90": round(float(np.percentile(k_each, 90)), 2),
+            "launches": int(k_launches),
             "bytes_per_launch": int(kernel_bytes),
         },
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "mean_with_kernel_events": round(ms_per_step_kt, 4)},
     }
     if not args.no_prefill:
         result["prefill"] = prefill_leg()

@@ -30,6 +30,7 @@ FLAG_PLAN_ONLY = 1
 
 OK, E_ARG, E_NOPAGE, E_WINDOW_FULL, E_WINDOW_SHORT, E_NUMERIC, E_HIP, E_WORKSPACE, E_STATE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 TIMED_DECODE, TIMED_WRITE = 0, 1  # kernels recorded by KVStore.set_timing
+TIMING_PAIRS = 4096               # event pairs per timed kernel
 _NAMES = {E_ARG: "E_ARG", E_NOPAGE: "E_NOPAGE", E_WINDOW_FULL: "E_WINDOW_FULL", E_WINDOW_SHORT: "E_WINDOW_SHORT",
           E_NUMERIC: "E_NUMERIC", E_HIP: "E_HIP", E_WORKSPACE: "E_WORKSPACE", E_STATE: "E_STATE"}
 
@@ -86,7 +87,7 @@ def load():
         "oscar_kv_set_decode_split": [P, I32],
         "oscar_kv_set_decode_kernel": [P, I32],
         "oscar_kv_set_timing": [P, I32],
-        "oscar_kv_read_timing": [P, I32, P, P],
+        "oscar_kv_read_timing": [P, I32, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -294,13 +295,15 @@ class KVStore:
         (measurement aid)."""
         _check(load().oscar_kv_set_timing(self.handle, int(bool(enable))))
 
-    def read_timing(self, kernel):
-        """(timed launches, summed milliseconds) of TIMED_DECODE or TIMED_WRITE since the last
-        read of that kernel; waits for them."""
+    def read_timing(self, kernel, each=False):
+        """(timed launches, summed milliseconds[, per-launch milliseconds]) of TIMED_DECODE or
+        TIMED_WRITE since the last read of that kernel; waits for them."""
         n = ctypes.c_int32(0)
         ms = ctypes.c_double(0.0)
-        _check(load().oscar_kv_read_timing(self.handle, int(kernel), ctypes.byref(n), ctypes.byref(ms)))
-        return n.value, ms.value
+        per = np.zeros(TIMING_PAIRS, dtype=np.float32) if each else None
+        _check(load().oscar_kv_read_timing(self.handle, int(kernel), ctypes.byref(n), ctypes.byref(ms),
+                                           per.ctypes.data_as(ctypes.c_void_p) if each else None))
+        return (n.value, ms.value, per[:n.value].copy()) if each else (n.value, ms.value)
 
     # ---- views of the device buffers (for tests and export)
     def pool_view(self):

@@ -562,7 +562,7 @@ int oscar_kv_set_timing(oscar_kv* kv, int32_t enable) {
   return OSCAR_OK;
 }
 
-int oscar_kv_read_timing(oscar_kv* kv, int32_t kernel, int32_t* launches, double* total_ms) {
+int oscar_kv_read_timing(oscar_kv* kv, int32_t kernel, int32_t* launches, double* total_ms, float* each_ms) {
   if (!kv || !launches || !total_ms || kernel < 0 || kernel > 1) {
     set_error("oscar_kv_read_timing: null argument or unknown kernel");
     return OSCAR_E_ARG;
@@ -575,6 +575,7 @@ int oscar_kv_read_timing(oscar_kv* kv, int32_t kernel, int32_t* launches, double
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, kv->timing_ev[kernel][2 * i], kv->timing_ev[kernel][2 * i + 1]);
     if (e != hipSuccess) return hip_fail(e, "oscar_kv_read_timing");
     sum += ms;
+    if (each_ms) each_ms[i] = ms;
   }
   *launches = kv->timing_used[kernel];
   *total_ms = sum;

@@ -297,10 +297,12 @@ int oscar_kv_set_decode_kernel(oscar_kv *kv, int32_t kernel);
 int oscar_kv_set_timing(oscar_kv *kv, int32_t enable);
 
 /* Waits for the pairs recorded for `kernel` (OSCAR_TIMED_*), writes the number of
- * timed launches to *launches and their summed duration in milliseconds to
- * *total_ms, and frees those pairs for reuse.  OSCAR_E_ARG for a null argument or
- * an unknown kernel, OSCAR_E_STATE when timing is off. */
-int oscar_kv_read_timing(oscar_kv *kv, int32_t kernel, int32_t *launches, double *total_ms);
+ * timed launches to *launches, their summed duration in milliseconds to
+ * *total_ms and, when each_ms is not NULL, each launch's duration in launch order
+ * to each_ms[0 .. *launches - 1] (room for OSCAR_TIMING_PAIRS entries), and frees
+ * those pairs for reuse.  OSCAR_E_ARG for a null argument or an unknown kernel,
+ * OSCAR_E_STATE when timing is off. */
+int oscar_kv_read_timing(oscar_kv *kv, int32_t kernel, int32_t *launches, double *total_ms, float *each_ms);
 
 const char *oscar_last_error(void);
 void oscar_kv_destroy(oscar_kv *kv);

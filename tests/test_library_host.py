@@ -202,3 +202,11 @@ def test_value_calibration_errors():
     with pytest.raises(oscar.OscarError) as e:
         oscar.oscar_fold_value_rotation(np.ones((4, 128), np.float32), np.ones((128, 4), np.float32), bad, 1, 1)
     assert e.value.status == oscar.E_NUMERIC
+
+
+def test_binding_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    consts = dict(re.findall(r"#define\s+(OSCAR_\w+)\s+(-?\d+)", src))
+    assert int(consts["OSCAR_TIMING_PAIRS"]) == oscar.TIMING_PAIRS
+    assert int(consts["OSCAR_TIMED_DECODE"]) == oscar.TIMED_DECODE
+    assert int(consts["OSCAR_TIMED_WRITE"]) == oscar.TIMED_WRITE
