@@ -131,6 +131,10 @@ __device__ inline float lane_max(float v) {
   return v;
 }
 
+// pointer into the global address space (loads through it are global, not flat, loads)
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
 __device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   v4u u = {a, b, c, d};
   return __builtin_bit_cast(v8h, u);
@@ -316,17 +320,24 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   const __attribute__((address_space(4))) int32_t* ptab_c =
       (const __attribute__((address_space(4))) int32_t*)(ptab);
   int id_next = ptab_c[first];
+  // a 32-bit lane offset from the page's uniform base keeps the metadata load in the
+  // scalar-base + vector-offset form (no 64-bit per-lane address held across the loop)
+  const uint32_t md_off = META_OFF + 16u * static_cast<uint32_t>(tok);
   auto load_page = [&](int lpn, Raw& r) {
     const int page = id_next;
     id_next = ptab_c[min(lpn + 1, last - 1)];
-    const uint8_t* blk = a.pool + static_cast<size_t>(page) * page_stride + head_off;
-    const v4u* kp = reinterpret_cast<const v4u*>(blk + KC_OFF) + lane;
-    const v4u* vp = reinterpret_cast<const v4u*>(blk + VC_OFF) + lane;
+    // the page base is wave-uniform: pin it to scalar registers so that the compiler cannot
+    // reassociate the lane offsets into loop-invariant 64-bit per-lane addresses
+    uint64_t base = reinterpret_cast<uint64_t>(a.pool + static_cast<size_t>(page) * page_stride + head_off);
+    asm volatile("" : "+s"(base));
+    const gptr<uint8_t> blk = reinterpret_cast<gptr<uint8_t>>(base);
+    const gptr<v4u> kp = reinterpret_cast<gptr<v4u>>(blk + KC_OFF) + lane;
+    const gptr<v4u> vp = reinterpret_cast<gptr<v4u>>(blk + VC_OFF) + lane;
     r.kc0 = __builtin_nontemporal_load(kp);
     r.kc1 = __builtin_nontemporal_load(kp + 64);
     r.vc0 = __builtin_nontemporal_load(vp);
     r.vc1 = __builtin_nontemporal_load(vp + 64);
-    r.md = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(blk + META_OFF) + tok);
+    r.md = __builtin_nontemporal_load(reinterpret_cast<gptr<v4u>>(blk + md_off));
   };
 
   // FULL (a compile-time tag): every token of the page holds a code, so no per-token masking
@@ -404,9 +415,12 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
       // oacc row 4 q4 + r: G <= 4 -> head r (lanes 0-31); G = 8 -> head 4 (q4 % 2) + r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        // values, not array elements, in the conditional: a conditional of two lvalues would
+        // select an address and leave alpha[] in private memory
+        const float a_lo = alpha[r % G], a_hi = alpha[(4 + r) % G];
         float al;
-        if (G == 8) al = (q4 & 1) ? alpha[(4 + r) % G] : alpha[r % G];
-        else al = (r < G) ? alpha[r % G] : 0.0f;
+        if (G == 8) al = (q4 & 1) ? a_hi : a_lo;
+        else al = (r < G) ? a_lo : 0.0f;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) oacc[ct][r] *= al;
       }
