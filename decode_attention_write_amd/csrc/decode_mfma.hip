@@ -19,14 +19,14 @@
 //   * P.V: f16 MFMA 16x16x32.  A value code c placed in mantissa bits e..e+1 of an
 //     f16 with zero exponent *is* the f16 denormal c * 2^(e-24); one mask gives two
 //     such operands per 32-bit word.  The per-position factor is folded into P
-//     (A operand = p * s * 2^(4-e), at most 65504 since p <= 1), so the product is
-//     exactly p s c 2^-20.  P is carried as an fp16 pair hi + lo (lo = the rounding
+//     (A operand = p * s * 2^(4-e-LAZY), at most 65504 since p <= 2^LAZY), so the product
+//     is exactly p s c 2^-(20+LAZY).  P is carried as an fp16 pair hi + lo (lo = the rounding
 //     residual), which keeps 22 bits of p * s: the output is a strongly cancelling
 //     sum, and a single fp16 P costs ~5e-4 relative error.  With GQA <= 4 the lo rows
 //     ride in the otherwise empty rows 8..15 of the same instruction.
 // Each wavefront walks the pages of one (sequence, KV head, split) with 128-bit loads
-// of the raw page block, keeps a running softmax max (rescaling only when a new max
-// appears), and writes an (m, l, o) partial for the split combine.
+// of the raw page block, keeps a lazy running softmax maximum (rescaling only when a score
+// exceeds it by more than 2^LAZY), and writes an (m, l, o) partial for the split combine.
 #include <type_traits>
 
 #include "common.h"
@@ -139,6 +139,14 @@ __device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   v4u u = {a, b, c, d};
   return __builtin_bit_cast(v8h, u);
 }
+
+// Lazy running maximum: a page only triggers the rescale when one of its scores exceeds the
+// running maximum by more than LAZY (log2 units).  Any reference value m gives the same
+// softmax once the partials are combined (the record carries m), so the maximum only has to
+// bound the exponentials: p = 2^(score - m) <= 2^LAZY, which the fp32 sums and the scaled
+// fp16 P operand absorb.  On random-key workloads the running maximum of a 150-page split rises
+// on about 11 % of the pages, by more than 2 on about 1 % (mostly the split's first page).
+constexpr int LAZY = 2;
 
 // Exponent e of the f16 denormal a value code lands in, by its position p' = 4 s + kk/2
 // within the 32-bit word (see the unpack in the page loop).
@@ -294,7 +302,8 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   // token of this lane after the Q.K row merge: tile order (0, 2, 1, 3) by 16-lane row
   const int tile = ((q4 & 1) << 1) | (q4 >> 1);
   const int tok = 16 * tile + n16;
-  const float pfac = __builtin_ldexpf(1.0f, 4 - vcode_exp(4 * (tok >> 5) + ((tok & 7) >> 1)));
+  // the extra 2^-LAZY keeps p * s * pfac within fp16 range while p may reach 2^LAZY
+  const float pfac = __builtin_ldexpf(1.0f, 4 - LAZY - vcode_exp(4 * (tok >> 5) + ((tok & 7) >> 1)));
 
   float m_run[G], l_acc[G], lo_acc[2][G];
 #pragma unroll
@@ -398,8 +407,9 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
       zmax = fmaxf(zmax, z[h]);
       x0[h] = sc;  // keep the score for the rescale path
     }
-    if (__any(zmax > 0.0f)) {
-      // a new maximum: rescale everything accumulated so far (rare after the first pages)
+    if (__any(zmax > static_cast<float>(LAZY))) {
+      // the running maximum is stale by more than 2^LAZY: move it to the exact maximum so far
+      // and rescale everything accumulated (in practice only on a split's first page)
       float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     const float f0 = sv0 * pfac, f1 = sv1 * pfac;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      // z <= 0 here; the raw exp2 flushes results below 2^-126 to zero, which is harmless
+      // z <= LAZY here; the raw exp2 flushes results below 2^-126 to zero, which is harmless
       const float p = valid ? __builtin_amdgcn_exp2f(z[h]) : 0.0f;
       l_acc[h] += p;
       lo_acc[0][h] = fmaf(p, lv0, lo_acc[0][h]);
@@ -535,7 +545,7 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     losum[0][h] = lane_sum(lo_acc[0][h]);
     losum[1][h] = lane_sum(lo_acc[1][h]);
   }
-  const float two20 = 1048576.0f;
+  const float two20 = __builtin_ldexpf(1.0f, 20 + LAZY);  // undoes pfac's 2^(e - 4 + LAZY)
   if (G <= 4) {
     // rows 8..15 (lanes 32..63) hold the lo-residual products of rows 0..7: fold them in
 #pragma unroll
