@@ -408,6 +408,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for st in stores:
             st.decode(seqs, qs[0], scale, out=outs[0], ws=ws)
+            st.set_timing(True)
         e0.record()
         for r in range(2):
             for l, st in enumerate(stores):
@@ -415,7 +416,12 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (2 * n_layers)
-        log(f"sweep pps={pps}: {us:.1f} us/layer, {2.085e9 / us / 1e3:.0f} GB/s")
+        k_n, k_ms = 0, 0.0
+        for st in stores:
+            n, ms = st.read_timing(oscar.TIMED_DECODE)
+            k_n, k_ms = k_n + n, k_ms + ms
+            st.set_timing(False)
+        log(f"sweep pps={pps}: split kernel {k_ms * 1e3 / max(k_n, 1):.1f} us, call {us:.1f} us/layer")
     for st in stores:
         st.set_decode_split(args.pps)
 

@@ -47,26 +47,27 @@ def _kernel_meta(lines):
 
 def _page_loops(lines, symbol):
     """Bodies of the kernel's outermost loops that stream INT2 pages: wide global loads feeding
-    matrix-core instructions (the BF16 sink/window loops use no matrix cores and wait per batch)."""
-    loops, start = [], None
-    for i, ln in enumerate(lines):
-        if ln.startswith(symbol + ":"):
-            start = i
-        elif start is not None and "s_endpgm" in ln:
-            break
-    assert start is not None, symbol
-    i = start
-    while i < len(lines) and "s_endpgm" not in lines[i]:
-        if "Loop Header: Depth=1" in lines[i]:
-            label = lines[i].split(":")[0]
-            j = i + 1
-            while not re.search(r"s_c?branch\w* " + re.escape(label) + r"$", lines[j]):
-                j += 1
-            body = lines[i:j + 1]
-            if any("global_load_dwordx4" in b for b in body) and any("v_mfma" in b for b in body):
-                loops.append(body)
-            i = j
-        i += 1
+    matrix-core instructions (the BF16 sink/window loops use no matrix cores and wait per batch).
+    A loop is its header block plus every block the compiler annotates as inside it."""
+    start = next(i for i, ln in enumerate(lines) if ln.startswith(symbol + ":"))
+    end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
+    blocks, cur = [], None
+    for ln in lines[start:end]:
+        if re.match(r"^\.LBB\d+_\d+:", ln):
+            cur = [ln]
+            blocks.append(cur)
+        elif cur is not None:
+            cur.append(ln)
+    loops = []
+    for b in blocks:
+        if "Loop Header: Depth=1" not in b[0]:
+            continue
+        name = b[0].split(":")[0][2:]  # .LBBx_y -> BBx_y
+        body = [ln for x in blocks
+                if x is b or f"Header={name} Depth=1" in x[0] or f"Parent Loop {name} Depth=1" in x[0]
+                for ln in x]
+        if any("global_load_dwordx4" in ln for ln in body) and any("v_mfma" in ln for ln in body):
+            loops.append(body)
     return loops
 
 
