@@ -246,6 +246,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 131072-token prefill-write leg")
     ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
     ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="fixed page range per split (no page sharing between the splits of a unit)")
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -294,6 +296,7 @@ def main():
         st.set_rotation(rots[l])
         st.set_decode_split(args.pps)
         st.set_decode_kernel(args.kernel)
+        st.set_decode_deterministic(args.deterministic)
         prm = sgpu.HeadParams(cfg, l, hkv)
         for s in range(B):
             sgpu.draw_kv(prm, s, 0, ctx, kbuf[0], vbuf[0])

@@ -38,7 +38,8 @@ EXPORTS = [
     "oscar_calibrate_host", "oscar_calibrate_value_host", "oscar_fold_value_rotation", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
-    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_timing",
+    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_decode_deterministic",
+    "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
 ]
 
@@ -86,6 +87,7 @@ def load():
         "oscar_kv_reset_seq": [P, I32, P],
         "oscar_kv_set_decode_split": [P, I32],
         "oscar_kv_set_decode_kernel": [P, I32],
+        "oscar_kv_set_decode_deterministic": [P, I32],
         "oscar_kv_set_timing": [P, I32],
         "oscar_kv_read_timing": [P, I32, P, P, P],
     }
@@ -289,6 +291,11 @@ class KVStore:
     def set_decode_kernel(self, kernel):
         """0 = matrix-core kernel (default), 1 = reference-grade fp32 kernel."""
         _check(load().oscar_kv_set_decode_kernel(self.handle, int(kernel)))
+
+    def set_decode_deterministic(self, on=True):
+        """Fixed page range per split (bitwise repeatable decode) instead of the default page
+        sharing between the splits of a (sequence, KV head)."""
+        _check(load().oscar_kv_set_decode_deterministic(self.handle, 1 if on else 0))
 
     def set_timing(self, enable=True):
         """Record HIP events around every launch of the decode split kernel and the write kernel

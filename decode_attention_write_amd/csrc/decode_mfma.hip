@@ -48,6 +48,26 @@ constexpr int QP_STRIDE = QPREP_STRIDE;
 __host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
   return static_cast<size_t>(a.n_seqs) * a.hq * a.n_split_max * PART_STRIDE * sizeof(float);
 }
+// Work sharing between the INT2 splits of one (sequence, KV head): the unit's full pages are
+// cut into groups of share_group<G>() pages, one group per step of the page loop.  Work-group
+// s starts on groups s and n_splits + s; every further group is handed out through one
+// counter per unit (set to 2 n_splits by the query preparation) by an atomic that a step
+// issues before its page loads and reads after its math, so the atomic returns while the step
+// runs.  All splits of the unit share the query and their records are merged by the same
+// softmax combine, so a record may cover any subset of the unit's pages; a work-group that the
+// hardware packs onto a busy SIMD, or starts late, simply ends up with fewer groups.  Every
+// step issues the same memory operations (the wait counts of the loop stay exact).  With
+// DecodeArgs::share = 0 (the deterministic mode) split s covers the fixed range
+// [s pps, min((s + 1) pps, full pages)) and its atomics add nothing.  A partially filled last
+// page, and the BF16 sink + window work when it is folded, belong to the last split and are
+// done before its page loop.
+template <int G>
+__host__ __device__ constexpr int share_group() { return G == 8 ? 2 : 3; }
+
+// Per (sequence of the chunk, KV head): one page counter per split.
+__host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
+  return qprep_offset(a) + static_cast<size_t>(a.n_seqs) * a.hkv * QP_STRIDE;
+}
 
 // ------------------------------------------------------------------ query preparation
 // Grid (KV heads, sequences of the chunk), 256 threads.
@@ -100,6 +120,10 @@ __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
     wc[3 * tid + 1] = qt[tid][0] * 128.0f / sig[tid];
     wc[3 * tid + 2] = qt[tid][1] * 128.0f / sig[tid];
   }
+  // group counter of the unit: the first two groups of every split are taken
+  int32_t* ctr = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(a.part) + counter_offset(a)) +
+                 (static_cast<size_t>(sl) * a.hkv + kvh) * a.n_split_max;
+  if (tid == 0) ctr[0] = 2 * int2_splits(sq.n_int2, a.pages_per_split);
   // A operands: head block hb, lane l: row m = l % 16 = 4 (2 tau + grp) + h4, K-step g covers
   // channels 64 g + 16 (l / 16) + j, j = 0..15 (byte j of the lane's 16 bytes)
   constexpr int HB = (G + 3) / 4;
@@ -147,6 +171,7 @@ __device__ inline v8h as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 // fp16 P operand absorb.  On random-key workloads the running maximum of a 150-page split rises
 // on about 11 % of the pages, by more than 2 on about 1 % (mostly the split's first page).
 constexpr int LAZY = 2;
+
 
 // Exponent e of the f16 denormal a value code lands in, by its position p' = 4 s + kk/2
 // within the 32-bit word (see the unpack in the page loop).
@@ -248,7 +273,13 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
 }
 
 // ------------------------------------------------------------------ INT2 page loop
-// Grid (splits, KV heads, sequences of the chunk), one wavefront per work-group.
+// Grid (KV heads x sequences of the chunk, splits), one wavefront per work-group.  Work-groups
+// are dispatched split by split, so every unit gets one work-group of each dispatch age (waves
+// of a SIMD issue oldest first, and with the unit slowest in the grid the units dispatched last
+// finished up to 50 % after the first); within a split the units are rotated by the split index,
+// so that with the dispatcher's round robin over the XCDs (linear index mod 8) the splits of a
+// unit land on different XCDs (units confined to one XCD finished up to 30 % apart, with the
+// XCDs' speeds).  The page sharing within a unit then evens out the rest.
 // Records 0 .. n_isplits-1 are INT2 page ranges, record n_isplits the BF16 sink + window.
 
 template <int G>
@@ -256,7 +287,10 @@ template <int G>
 __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a) {
   constexpr int GP = G < 4 ? 4 : G;       // heads padded to a multiple of 4
   constexpr int HB = GP / 4;              // head blocks (MFMA row blocks of Q.K)
-  const int split = blockIdx.x, kvh = blockIdx.y, sl = blockIdx.z;
+  const int n_units = a.hkv * a.n_seqs;
+  const int split = blockIdx.y;
+  const int unit = (static_cast<int>(blockIdx.x) + n_units - split % n_units) % n_units;
+  const int kvh = unit % a.hkv, sl = unit / a.hkv;
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
   const DecodeSeq sq = a.seqs[sl];
   const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
@@ -299,9 +333,8 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   for (int i = lane; i < 32 * 64; i += 64) (&plds[0][0])[i] = static_cast<_Float16>(0.0f);
   constexpr int LO_ROWS = (G == 8) ? 16 : 8;
 
-  // token of this lane after the Q.K row merge: tile order (0, 2, 1, 3) by 16-lane row
-  const int tile = ((q4 & 1) << 1) | (q4 >> 1);
-  const int tok = 16 * tile + n16;
+  // token of this lane after the Q.K row merge (which pairs tiles 0/2 and 1/3): the lane index
+  const int tok = lane;
   // the extra 2^-LAZY keeps p * s * pfac within fp16 range while p may reach 2^LAZY
   const float pfac = __builtin_ldexpf(1.0f, 4 - LAZY - vcode_exp(4 * (tok >> 5) + ((tok & 7) >> 1)));
 
@@ -314,7 +347,6 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   for (int ct = 0; ct < 8; ++ct) oacc[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int first = split * a.pages_per_split;
-  const int last = min(first + a.pages_per_split, n_pages);
   const int32_t* ptab = a.page_table + static_cast<size_t>(sq.seq) * a.max_pages;
   const size_t head_off = static_cast<size_t>(kvh) * HEAD_BLOCK;
   const size_t page_stride = static_cast<size_t>(a.hkv) * HEAD_BLOCK;
@@ -328,13 +360,7 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   struct Raw { v4u kc0, kc1, vc0, vc1, md; };
   const __attribute__((address_space(4))) int32_t* ptab_c =
       (const __attribute__((address_space(4))) int32_t*)(ptab);
-  int id_next = ptab_c[first];
-  // a 32-bit lane offset from the page's uniform base keeps the metadata load in the
-  // scalar-base + vector-offset form (no 64-bit per-lane address held across the loop)
-  const uint32_t md_off = META_OFF + 16u * static_cast<uint32_t>(tok);
-  auto load_page = [&](int lpn, Raw& r) {
-    const int page = id_next;
-    id_next = ptab_c[min(lpn + 1, last - 1)];
+  auto load_block = [&](int page, Raw& r) {
     // the page base is wave-uniform: pin it to scalar registers so that the compiler cannot
     // reassociate the lane offsets into loop-invariant 64-bit per-lane addresses
     uint64_t base = reinterpret_cast<uint64_t>(a.pool + static_cast<size_t>(page) * page_stride + head_off);
@@ -346,7 +372,10 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     r.kc1 = __builtin_nontemporal_load(kp + 64);
     r.vc0 = __builtin_nontemporal_load(vp);
     r.vc1 = __builtin_nontemporal_load(vp + 64);
-    r.md = __builtin_nontemporal_load(reinterpret_cast<gptr<v4u>>(blk + md_off));
+    // the metadata base past the immediate-offset range gets its own scalar pair
+    uint64_t base_md = base + META_OFF;
+    asm volatile("" : "+s"(base_md));
+    r.md = __builtin_nontemporal_load(reinterpret_cast<gptr<v4u>>(base_md) + lane);  // token = lane
   };
 
   // FULL (a compile-time tag): every token of the page holds a code, so no per-token masking
@@ -376,17 +405,22 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
         }
       }
     }
-    // ---- merge rows across lanes: afterwards lane = token `tok`, x0/x1 = group 0/1 dot per head
+    // ---- merge rows across lanes: afterwards lane = token, x0/x1 = group 0/1 dot per head.
+    // Lane group q4 holds rows (tau, grp) = (q4 / 2, q4 % 2).  The 32-lane swaps of tiles 0/2
+    // and 1/3 put the tau = 0 rows of both tiles of a pair in one register and the tau = 1 rows
+    // in the other (lanes 0-31 the first tile, 32-63 the second); the two terms are merged in
+    // integers; the 16-lane swap then separates the groups, leaving tiles 0, 1, 2, 3 in lanes
+    // 0-15, 16-31, 32-47, 48-63.
     float x0[GP], x1[GP];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const auto s01 = __builtin_amdgcn_permlane32_swap(acc[hb][0][r], acc[hb][1][r], false, false);
-        const auto s23 = __builtin_amdgcn_permlane32_swap(acc[hb][2][r], acc[hb][3][r], false, false);
-        const int c01 = static_cast<int>((static_cast<uint32_t>(s01[0]) << 7) + static_cast<uint32_t>(s01[1]));
-        const int c23 = static_cast<int>((static_cast<uint32_t>(s23[0]) << 7) + static_cast<uint32_t>(s23[1]));
-        const auto gg = __builtin_amdgcn_permlane16_swap(c01, c23, false, false);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(acc[hb][0][r], acc[hb][2][r], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(acc[hb][1][r], acc[hb][3][r], false, false);
+        const int c02 = static_cast<int>((static_cast<uint32_t>(s02[0]) << 7) + static_cast<uint32_t>(s02[1]));
+        const int c13 = static_cast<int>((static_cast<uint32_t>(s13[0]) << 7) + static_cast<uint32_t>(s13[1]));
+        const auto gg = __builtin_amdgcn_permlane16_swap(c02, c13, false, false);
         x0[4 * hb + r] = static_cast<float>(static_cast<int>(gg[0]));
         x1[4 * hb + r] = static_cast<float>(static_cast<int>(gg[1]));
       }
@@ -484,56 +518,130 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     }
   };
 
-  if (first < last) {
-    // NBUF rotating register sets: NBUF - 1 pages in flight while one is processed (two for
-    // GQA <= 4; one for GQA 8, whose registers are taken by its wider P.V operands)
-    // pages [first, last_full) are full; a partially filled last page of the sequence is
-    // handled after the main loop, with masking
-    const int last_full = (last == n_pages && (sq.n_int2 % PAGE) != 0) ? last - 1 : last;
+  // the last split's extra work first: the BF16 sink + window records (when folded) and the
+  // partially filled last page; then every vector-memory access has returned, so the page
+  // loop starts from a clean wait state
+  if (split == n_isplits - 1) {
+    if (fold)
+      bf16_split<G>(a, sq, kvh, sl, n_isplits, 0, RING_CHUNKS, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+    if (sq.n_int2 % PAGE != 0) {
+      Raw b;
+      load_block(ptab_c[sq.n_int2 / PAGE], b);
+      process_page(sq.n_int2 / PAGE, b, std::false_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // ---- the page stream of this work-group (work sharing within the unit, see share_group):
+  // groups of NB consecutive full pages, one group per loop step
+  constexpr int NB = share_group<G>();      // rotating register sets = pages per step
+  const int n_full = sq.n_int2 / PAGE;
+  const int pps = a.pages_per_split;
+  int32_t* ctr = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(a.part) + counter_offset(a)) +
+                 (static_cast<size_t>(sl) * a.hkv + kvh) * a.n_split_max;
+  const int inc = a.share ? 1 : 0;
+  int pend = 0;      // lane 0: the group index the step's claim returned
+  auto claim = [&]() {
+    int old = 0;
+    if (lane == 0) {
+      // a per-lane address for the compiler: a wave-uniform one would let it broadcast the
+      // result right away (a full wait on the vector-memory counter)
+      uint64_t p = reinterpret_cast<uint64_t>(ctr);
+      asm volatile("" : "+v"(p));
+      old = __hip_atomic_fetch_add(reinterpret_cast<__attribute__((address_space(1))) int32_t*>(p), inc,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    pend = old;
+  };
+  // a group: first page and page count (0: nothing left)
+  auto group = [&](int g, int& g_first, int& g_n) {
+    g_first = __builtin_amdgcn_readfirstlane(g * NB);
+    g_n = __builtin_amdgcn_readfirstlane(max(0, min(NB, n_full - g * NB)));
+  };
+  const int own_end = min(first + pps, n_full);   // the deterministic mode's range
+  int det_next = first + 2 * NB;
+  // the group after the next one: the claimed group, or the next of the fixed range
+  auto resolve = [&](int& g_first, int& g_n) {
+    if (a.share) {
+      group(__builtin_amdgcn_readfirstlane(pend), g_first, g_n);
+    } else {
+      g_first = det_next;
+      g_n = max(0, min(NB, own_end - det_next));
+      det_next += NB;
+    }
+  };
+  int t_first, t_n, n_first, n_n;
+  if (a.share) {
+    group(split, t_first, t_n);
+    group(n_isplits + split, n_first, n_n);
+  } else {
+    t_first = first;
+    t_n = max(0, min(NB, own_end - first));
+    n_first = first + NB;
+    n_n = max(0, min(NB, own_end - first - NB));
+  }
+  // page ids of a group (a missing page repeats the previous id, so every step issues the same
+  // loads and the wait counts stay exact); the third id is unused when NB = 2
+  int last_id = ptab_c[(t_n > 0) ? t_first : 0];
+  auto group_ids = [&](int g_first, int g_n, int& i0, int& i1, int& i2) {
+    i0 = (g_n > 0) ? ptab_c[g_first] : last_id;
+    i1 = (g_n > 1) ? ptab_c[g_first + 1] : i0;
+    i2 = (NB > 2 && g_n > 2) ? ptab_c[g_first + 2] : i1;
+    last_id = (NB > 2) ? i2 : i1;
+  };
+  int t0, t1, t2, n0, n1, n2;
+  group_ids(t_first, t_n, t0, t1, t2);
+  group_ids(n_first, n_n, n0, n1, n2);
+
+  {
+    // NB rotating register sets: NB - 1 pages in flight while one is processed (two for
+    // GQA <= 4; one for GQA 8, whose registers are taken by its wider P.V operands).  One step
+    // processes the current group t and loads the next group n; the loop has a single exit.
     const std::true_type full{};
-    const std::false_type masked{};
-    if constexpr (G == 8) {
+    if constexpr (NB == 2) {
       Raw b0, b1;
-      load_page(first, b0);
+      load_block(t0, b0);
       __builtin_amdgcn_sched_barrier(0);
-      int lp = first;
-      for (; lp + 2 <= last_full; lp += 2) {
-        load_page(lp + 1, b1);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
-        process_page(lp, b0, full);
-        load_page(min(lp + 2, last - 1), b0);
-        __builtin_amdgcn_sched_barrier(0);
-        process_page(lp + 1, b1, full);
+      if (t_n > 0) {
+        do {
+          load_block(t1, b1);
+          claim();  // after the load: processing b0 then waits for b0 only
+          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
+          process_page(0, b0, full);
+          load_block(n0, b0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t_n > 1) process_page(0, b1, full);
+          t_n = n_n;
+          t0 = n0;
+          t1 = n1;
+          resolve(n_first, n_n);
+          group_ids(n_first, n_n, n0, n1, n2);
+        } while (t_n > 0);
       }
-      // at most one full page and the partial page left; b0 holds page lp
-      if (lp + 1 < last) load_page(lp + 1, b1);
-      if (lp < last) process_page(lp, b0, masked);
-      if (lp + 1 < last) process_page(lp + 1, b1, masked);
     } else {
       Raw b0, b1, b2;
-      load_page(first, b0);
+      load_block(t0, b0);
       __builtin_amdgcn_sched_barrier(0);  // keep page order in the queue: waits stay vmcnt(10)
-      load_page(min(first + 1, last - 1), b1);
+      load_block(t1, b1);
       __builtin_amdgcn_sched_barrier(0);
-      int lp = first;
-      for (; lp + 3 <= last_full; lp += 3) {
-        load_page(lp + 2, b2);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
-        process_page(lp, b0, full);
-        load_page(min(lp + 3, last - 1), b0);
-        __builtin_amdgcn_sched_barrier(0);
-        process_page(lp + 1, b1, full);
-        load_page(min(lp + 4, last - 1), b1);
-        __builtin_amdgcn_sched_barrier(0);
-        process_page(lp + 2, b2, full);
+      if (t_n > 0) {
+        do {
+          claim();
+          load_block(t2, b2);
+          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
+          process_page(0, b0, full);
+          load_block(n0, b0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t_n > 1) process_page(0, b1, full);
+          load_block(n1, b1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t_n > 2) process_page(0, b2, full);
+          t_n = n_n;
+          t2 = n2;
+          resolve(n_first, n_n);
+          group_ids(n_first, n_n, n0, n1, n2);
+        } while (t_n > 0);
       }
-      // up to two full pages and the partial page left; b0 and b1 hold pages lp and lp + 1
-      // (the loop has no early exit: an exit edge would merge wait states and force a full
-      // drain of the prefetch at the loop head)
-      if (lp < last) process_page(lp, b0, masked);
-      if (lp + 2 < last) load_page(lp + 2, b0);   // b0 is free again: two register sets suffice
-      if (lp + 1 < last) process_page(lp + 1, b1, masked);
-      if (lp + 2 < last) process_page(lp + 2, b0, masked);
     }
   }
 
@@ -575,8 +683,6 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
       }
     }
   }
-  if (fold && split == n_isplits - 1)
-    bf16_split<G>(a, sq, kvh, sl, n_isplits, 0, RING_CHUNKS, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
 }
 
 // Work-groups to plan for one residency round: all wave slots of the device but one per
@@ -620,7 +726,7 @@ static hipError_t launch_g(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hi
     const hipError_t e = hipEventRecord(t0, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_decode_mfma<G>, dim3(a.n_split_max, a.hkv, a.n_seqs), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_decode_mfma<G>, dim3(a.hkv * a.n_seqs, a.n_split_max), dim3(64), 0, s, a);
   if (t1) {
     const hipError_t e = hipEventRecord(t1, s);
     if (e != hipSuccess) return e;

@@ -76,6 +76,7 @@ struct DecodeArgs {
   int32_t pages_per_split, n_split_max;
   float scale_log2;       // sm_scale * log2(e)
   int32_t kernel;         // 0 matrix-core split kernel, 1 reference kernel (record layout)
+  int32_t share;          // matrix-core kernel: 1 = splits of a unit share their pages, 0 = fixed ranges
   DecodeSeq seqs[CHUNK];
 };
 

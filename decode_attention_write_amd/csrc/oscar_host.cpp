@@ -45,6 +45,7 @@ struct oscar_kv {
   std::deque<int32_t> fifo;
   int32_t pages_per_split = 0;
   int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
+  int32_t deterministic = 0;   // 1: fixed page range per split (no sharing between splits)
   bool has_rotation = false;
   // timing events per timed kernel: 2 * OSCAR_TIMING_PAIRS each when timing is on
   std::vector<hipEvent_t> timing_ev[2];
@@ -435,8 +436,10 @@ int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int
                                                           static_cast<int>(pps), kv->decode_kernel));
   }
   const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
+  // split partials, then the prepared queries, then one page counter per split (matrix-core kernel)
   *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float) +
-           static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE;
+           static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE +
+           static_cast<size_t>(rows) * kv->desc.num_kv_heads * max_split * sizeof(int32_t);
   return OSCAR_OK;
 }
 
@@ -483,6 +486,7 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     }
     a.n_split_max = static_cast<int32_t>(max_split);
     a.kernel = kv->decode_kernel;
+    a.share = kv->deterministic ? 0 : 1;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
     hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st, t0, t1) : launch_decode_mfma(a, st, t0, t1);
@@ -526,6 +530,12 @@ int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, void* stream) {
   kv->len[seq] = 0;
   kv->n_int2[seq] = 0;
   return push_table(kv, upd, as_stream(stream));
+}
+
+int oscar_kv_set_decode_deterministic(oscar_kv* kv, int32_t on) {
+  if (!kv || (on != 0 && on != 1)) { set_error("oscar_kv_set_decode_deterministic: on must be 0 or 1"); return OSCAR_E_ARG; }
+  kv->deterministic = on;
+  return OSCAR_OK;
 }
 
 int oscar_kv_set_decode_kernel(oscar_kv* kv, int32_t kernel) {

@@ -239,7 +239,7 @@ int oscar_kv_evict_window(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, 
                           void *stream);
 
 /* Device workspace bytes oscar_decode_attn needs for these sequences in their
- * current state (split-K partials). */
+ * current state (split-K partials, prepared queries, per-split page counters). */
 int oscar_decode_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs,
                                  size_t *bytes);
 
@@ -273,6 +273,17 @@ int oscar_kv_reset_seq(oscar_kv *kv, int32_t seq, void *stream);
 
 /* Decode tuning: pages_per_split = 0 picks a split size from the batch. */
 int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);
+
+/* Decode reproducibility.  on = 0 (default): the INT2 splits of one (sequence,
+ * KV head) share their pages at run time (a split that finishes early takes page
+ * groups of the others), which evens out the finishing times of the work-groups;
+ * which pages land in which partial record then varies between calls, and so do
+ * the outputs, by the rounding of p * s to the fp16 pair relative to each record's
+ * running maximum (about 1e-5 relative, bounded by the same 1e-3 parity bound).
+ * on = 1: every split covers a fixed page range, and repeated calls on the same
+ * state give bitwise identical outputs for a given split size.  The reference
+ * kernel (1) is always deterministic.  OSCAR_E_ARG unless on is 0 or 1. */
+int oscar_kv_set_decode_deterministic(oscar_kv *kv, int32_t on);
 
 /* Decode kernel: 0 (default) = the matrix-core kernel (i8 MFMA for q.k on the raw
  * codes, f16 MFMA for p.v); 1 = the reference-grade kernel that dequantizes every

@@ -252,6 +252,7 @@ def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
         free = np.arange(80) if order == "identity" else synth.page_permutation(synth.CFG_QWEN3_4B, 3, 80)
         st = _store(gpu_lib, hq, hkv, 2, 40, 80, free, rot)
         st.set_decode_kernel(kernel)
+        st.set_decode_deterministic(True)
         st.write([0, 1], parity.to_dev_bf16(ks), parity.to_dev_bf16(vs))
         # 38 INT2 pages + 320 BF16 tokens (weight 32 pages): 35 and 70 pages per split leave room
         # for the BF16 work in the last INT2 split (folded); 1, 3 and 38 give it its own work-group
@@ -265,6 +266,13 @@ def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
         n_timed, ms = st.read_timing(gpu_lib.TIMED_DECODE)
         assert n_timed == 12 and ms > 0.0
         st.set_timing(False)
+        # the default page sharing between splits: same result up to the rounding of p * s
+        st.set_decode_deterministic(False)
+        for pps in (1, 3, 35, 0):
+            st.set_decode_split(pps)
+            for _ in range(3):
+                o = st.decode([0, 1], q, SCALE).cpu().numpy()
+                assert parity.rel_l2(o, outs[(order, pps)]) <= (1e-6 if kernel == 1 else 1e-4), pps
         gpu = parity.export(st)
         lens = np.array([L, L])
         iso = attention.decode(gpu[0], gpu[1], gpu[2], lens, lens - 320, rot, qb, [0, 1], SCALE, hq)

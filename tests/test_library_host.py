@@ -127,21 +127,33 @@ def test_workspace_bytes_and_split_choice():
     s.write([0], None, None, n_new=320 + 64 * 20)
     s.write([1], None, None, n_new=100)
     qprep = 2 * 2 * 8448          # prepared-query area: 2 seqs x 2 KV heads
+
+    def expect(records):
+        # partials (2 seqs x 8 q heads x records x 130 floats), prepared queries, and one int32
+        # page counter per split of each (seq, KV head)
+        return 2 * 8 * records * 130 * 4 + qprep + 2 * 2 * records * 4
+
     nb = s.workspace_bytes([0, 1])
-    assert nb > qprep and (nb - qprep) % (130 * 4) == 0
+    assert nb > qprep and (nb - qprep) % (130 * 4 * 8 * 2 + 2 * 2 * 4) == 0
     s.set_decode_split(4)
     nb4 = s.workspace_bytes([0, 1])
     # sequence 0: 20 pages / 4 per split = 5 INT2 records; its 320 BF16 tokens weigh 32 pages,
     # cut into min(5, ceil(32 / 4)) = 5 chunk ranges -> 10 records.  Sequence 1 (100 tokens, no
-    # INT2): weight 10 -> ceil(10 / 4) = 3 records.  2 seqs x 8 q heads x 10 records x 130 floats
-    assert nb4 == 2 * 8 * 10 * 130 * 4 + qprep
+    # INT2): weight 10 -> ceil(10 / 4) = 3 records.
+    assert nb4 == expect(10)
     s.set_decode_split(40)
     # 1 INT2 record + 1 BF16 record (weight 32 <= 40 pages per split)
-    assert s.workspace_bytes([0, 1]) == 2 * 8 * 2 * 130 * 4 + qprep
+    assert s.workspace_bytes([0, 1]) == expect(2)
     s.set_decode_kernel(1)
     s.set_decode_split(4)
     # the reference kernel keeps one BF16 record per unit: 5 + 1
-    assert s.workspace_bytes([0, 1]) == 2 * 8 * 6 * 130 * 4 + qprep
+    assert s.workspace_bytes([0, 1]) == expect(6)
+    s.set_decode_deterministic(True)   # the page-sharing switch does not change the plan
+    assert s.workspace_bytes([0, 1]) == expect(6)
+    for bad in (-1, 2):
+        with pytest.raises(oscar.OscarError) as e:
+            oscar._check(oscar.load().oscar_kv_set_decode_deterministic(s.handle, bad))
+        assert e.value.status == oscar.E_ARG
 
 
 def test_timing_errors():
