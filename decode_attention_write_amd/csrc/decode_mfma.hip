@@ -59,8 +59,8 @@ __host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
 // step issues the same memory operations (the wait counts of the loop stay exact).  With
 // DecodeArgs::share = 0 (the deterministic mode) split s covers the fixed range
 // [s pps, min((s + 1) pps, full pages)) and its atomics add nothing.  A partially filled last
-// page, and the BF16 sink + window work when it is folded, belong to the last split and are
-// done before its page loop.
+// page, and the BF16 sink + window work when it is folded, belong to split 0 and are done
+// before its page loop.
 template <int G>
 __host__ __device__ constexpr int share_group() { return G == 8 ? 2 : 3; }
 
@@ -288,18 +288,22 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   constexpr int GP = G < 4 ? 4 : G;       // heads padded to a multiple of 4
   constexpr int HB = GP / 4;              // head blocks (MFMA row blocks of Q.K)
   const int n_units = a.hkv * a.n_seqs;
-  const int split = blockIdx.y;
-  const int unit = (static_cast<int>(blockIdx.x) + n_units - split % n_units) % n_units;
+  const int y = blockIdx.y;   // the unit's work-group index, in dispatch order
+  const int unit = (static_cast<int>(blockIdx.x) + n_units - y % n_units) % n_units;
   const int kvh = unit % a.hkv, sl = unit / a.hkv;
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
   const DecodeSeq sq = a.seqs[sl];
   const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
   const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
   const int n_bsplits = bf16_splits(sq.n_int2, sq.len, a.pages_per_split, 0);
-  // the BF16 sink + window tokens (partial records n_isplits ..) ride on the last INT2 split
-  // when it has room for them, else they are work-groups n_isplits .. n_isplits + n_bsplits - 1
+  // the BF16 sink + window tokens (partial records n_isplits ..) are done first by INT2 split 0
+  // (the unit's oldest work-group) when the plan folds them, else by work-groups of their own,
+  // dispatched before the INT2 splits: work-groups dispatched last issue last and would finish
+  // last with work that nobody can share
   const bool fold = bf16_folded(sq.n_int2, sq.len, a.pages_per_split, 0);
-  if (split >= n_isplits + (fold ? 0 : n_bsplits)) return;
+  const int nbw = fold ? 0 : n_bsplits;
+  if (y >= n_isplits + nbw) return;
+  const int split = y - nbw;  // INT2 split; negative for a BF16 work-group
 
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
                       (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
@@ -307,9 +311,9 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   // P operand staging: hi rows (group, head) then lo rows; GQA <= 4: hi 0..7, lo 8..15,
   // GQA 8: hi 0..15, lo 16..31
   __shared__ _Float16 plds[32][64];
-  if (split >= n_isplits) {
-    const int b = split - n_isplits;
-    bf16_split<G>(a, sq, kvh, sl, split, (RING_CHUNKS * b) / n_bsplits, (RING_CHUNKS * (b + 1)) / n_bsplits,
+  if (split < 0) {
+    const int b = y;
+    bf16_split<G>(a, sq, kvh, sl, n_isplits + b, (RING_CHUNKS * b) / n_bsplits, (RING_CHUNKS * (b + 1)) / n_bsplits,
                   reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
     return;
   }
@@ -518,10 +522,10 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
     }
   };
 
-  // the last split's extra work first: the BF16 sink + window records (when folded) and the
-  // partially filled last page; then every vector-memory access has returned, so the page
-  // loop starts from a clean wait state
-  if (split == n_isplits - 1) {
+  // split 0's extra work first: the BF16 sink + window records (when folded) and the partially
+  // filled last page; then every vector-memory access has returned, so the page loop starts
+  // from a clean wait state
+  if (split == 0) {
     if (fold)
       bf16_split<G>(a, sq, kvh, sl, n_isplits, 0, RING_CHUNKS, reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
     if (sq.n_int2 % PAGE != 0) {

@@ -88,9 +88,10 @@ constexpr int PART_STRIDE = 130;
 // number of INT2 splits: a BF16 token moves 512 bytes (key and value rows), an INT2 page 5120,
 // so ten BF16 tokens weigh one page, and the BF16 work is cut into nb = ceil(weight / pps)
 // (1..5) work-groups of whole chunks so that none of them outweighs an INT2 split.  On the
-// matrix-core path (kernel 0) a single BF16 work-group rides on the last INT2 split when that
-// split's spare capacity holds its weight.  The reference kernel (kernel 1) keeps one BF16
-// work-group.
+// matrix-core path (kernel 0) a single BF16 work-group is folded into the INT2 work when the
+// last split's spare capacity (splits x pages-per-split - pages) holds its weight; that kernel
+// shares pages between the splits of a unit and gives the folded work to split 0.  The
+// reference kernel (kernel 1) keeps one BF16 work-group.
 constexpr int RING_CHUNKS = 5;
 __host__ __device__ inline int bf16_page_weight(int n_bf16) { return (n_bf16 + 9) / 10; }
 __host__ __device__ inline int int2_splits(int n_int2, int pps) { return ((n_int2 + 63) / 64 + pps - 1) / pps; }
