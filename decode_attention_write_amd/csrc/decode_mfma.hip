@@ -84,14 +84,27 @@ __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
   __shared__ float qin[G][D];
   for (int idx = tid; idx < G * D; idx += 256) qin[idx / D][idx % D] = bf16_to_f32(q[idx]);
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, c = idx % D;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-    for (int i = 0; i < D; i += 4)
+  {
+    // q' = q R: thread (half, c) reads column c of rows [64 half, 64 half + 64) once (coalesced,
+    // 32 loads in flight) for all G heads; the two halves are added through LDS
+    __shared__ float part[2][G][D];
+    const int c = tid & (D - 1), half = tid >> 7;
+    float acc[G];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fmaf(qin[h][i + u], rot[(i + u) * D + c], acc[u]);
-    qf[h][c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * a.scale_log2;
+    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+#pragma unroll 32
+    for (int i = 64 * half; i < 64 * half + 64; ++i) {
+      const float r = rot[i * D + c];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = fmaf(qin[h][i], r, acc[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) part[half][h][c] = acc[h];
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int h = idx / D, cc = idx % D;
+      qf[h][cc] = (part[0][h][cc] + part[1][h][cc]) * a.scale_log2;
+    }
   }
   __syncthreads();
   for (int h = tid >> 6; h < G; h += 4) {
