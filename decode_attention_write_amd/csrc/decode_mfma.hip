@@ -81,23 +81,25 @@ __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
   const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
   const uint16_t* q = a.q + (static_cast<size_t>(sq.src) * a.hq + static_cast<size_t>(kvh) * G) * D;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.part) + qprep_offset(a) + (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
+  // q' = q R: thread (half, c) reads column c of rows [64 half, 64 half + 64) once (coalesced)
+  // for all G heads; its 64 loads are issued before the query is staged, so the two latencies
+  // overlap; the two halves are added through LDS
+  const int c = tid & (D - 1), half = tid >> 7;
+  float rcol[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) rcol[i] = rot[(64 * half + i) * D + c];
   __shared__ float qin[G][D];
   for (int idx = tid; idx < G * D; idx += 256) qin[idx / D][idx % D] = bf16_to_f32(q[idx]);
   __syncthreads();
   {
-    // q' = q R: thread (half, c) reads column c of rows [64 half, 64 half + 64) once (coalesced,
-    // 32 loads in flight) for all G heads; the two halves are added through LDS
     __shared__ float part[2][G][D];
-    const int c = tid & (D - 1), half = tid >> 7;
     float acc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-#pragma unroll 32
-    for (int i = 64 * half; i < 64 * half + 64; ++i) {
-      const float r = rot[i * D + c];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(qin[h][i], r, acc[h]);
-    }
+    for (int i = 0; i < 64; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = fmaf(qin[h][64 * half + i], rcol[i], acc[h]);
 #pragma unroll
     for (int h = 0; h < G; ++h) part[half][h][c] = acc[h];
     __syncthreads();
