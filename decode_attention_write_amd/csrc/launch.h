@@ -41,6 +41,7 @@ struct WriteArgs {
   const int32_t* page_table;
   const uint8_t* rot;
   int32_t hkv, max_pages, n_new, n_seqs;
+  int32_t tiles_per_wg;  // k_write: 64-position tiles per work-group (set by launch_write)
   WriteSeq seqs[CHUNK];
 };
 

@@ -6,6 +6,8 @@
 // is rotated by R_K, clipped with c_K = 0.96 (values c_V = 0.92), quantized per
 // token to asymmetric INT2 in 64-channel groups; recent tokens stay BF16
 // (section "Together AI, INT2 KV 캐시 시스템 'OSCAR' 공개").
+#include <algorithm>
+
 #include "common.h"
 
 namespace oscar {
@@ -46,16 +48,16 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ write kernel
-// Grid (groups of WRITE_TILES tiles of 64 positions, KV heads, sequences of this chunk); 256
+// Grid (groups of tiles_per_wg tiles of 64 positions, KV heads, sequences of this chunk); 256
 // threads.  Tile i covers positions len0 + 64 i ... of its sequence.  For a sequence that was
-// empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.
+// empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.  launch_write sizes the groups
+// so that all work-groups are resident at once (one residency round: no partial last round).
 //
 // Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_bf16.  The
 // A operand is R^T as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0) (|R - r0 - r1| <= 2^-18 |R|),
 // the B operand the bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
 // its R^T operands in registers for all tiles of the work-group.
 
-constexpr int WRITE_TILES = 8;
 constexpr int XS = D + 4;  // fp32 row stride of the rotated tile (16-byte aligned rows)
 constexpr int KS = D + 8;  // bf16 row stride of the key tile
 
@@ -68,9 +70,9 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q4 = lane >> 4, n16 = lane & 15;
   const WriteSeq sq = a.seqs[sl];
   const int n_tiles = (a.n_new + PAGE - 1) / PAGE;
-  const int tile0 = blockIdx.x * WRITE_TILES;
+  const int tile0 = blockIdx.x * a.tiles_per_wg;
   if (tile0 >= n_tiles) return;
-  const int tile1 = min(tile0 + WRITE_TILES, n_tiles);
+  const int tile1 = min(tile0 + a.tiles_per_wg, n_tiles);
   const int len = sq.len0 + a.n_new;
   const int n_int2 = (sq.len0 == 0) ? max(0, len - RING) : 0;  // INT2 tokens of this call
 
@@ -241,8 +243,26 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
   }
 }
 
-hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s) {
-  const int groups = (n_tiles + WRITE_TILES - 1) / WRITE_TILES;
+// Work-groups of k_write that the device holds at once (occupancy query, cached per device).
+static int write_resident_workgroups() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n_cu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_write, 256, 0) != hipSuccess) return 0;
+    cache[dev] = n_cu * per_cu;
+  }
+  return cache[dev];
+}
+
+hipError_t launch_write(const WriteArgs& a_in, int n_tiles, hipStream_t s) {
+  WriteArgs a = a_in;
+  const int64_t total = static_cast<int64_t>(n_tiles) * a.hkv * a.n_seqs;
+  const int slots = write_resident_workgroups();
+  a.tiles_per_wg = slots > 0 ? static_cast<int32_t>(std::max<int64_t>(1, (total + slots - 1) / slots)) : 8;
+  const int groups = (n_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
   hipLaunchKernelGGL(k_write, dim3(groups, a.hkv, a.n_seqs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
