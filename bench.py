@@ -7,8 +7,9 @@ head_dim 128), batch 32, 100000-token context per sequence, INT2 history with a 
 are synthetic (seeded, drawn on the GPU); rotations are calibrated per (layer, KV head) from
 seeded queries.
 
-One step = for every layer: evict the oldest window token of each sequence into INT2, append
-one new token per sequence, run decode attention for all 32 query heads.  Prints one JSON
+One step = for every layer: the decode-step write (evict the oldest window token of each
+sequence into INT2, append one new token per sequence; one launch), then decode attention for
+all 32 query heads.  Prints one JSON
 line (stdout); progress goes to stderr.
 """
 import argparse
@@ -203,8 +204,7 @@ def prefill_leg(reps=5):
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for i in range(PREFILL_APPENDS):
-        st.evict([0], 1)
-        st.write([0], kbuf[:, L + i:L + i + 1], vbuf[:, L + i:L + i + 1])
+        st.decode_write([0], kbuf[:, L + i], vbuf[:, L + i])
     a1.record()
     torch.cuda.synchronize()
     st.set_timing(False)
@@ -249,6 +249,8 @@ def main():
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed page range per split (no page sharing between the splits of a unit)")
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write each step with the eviction and the append as two calls (comparison)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -334,8 +336,11 @@ def main():
     def step(i):
         for l in range(n_layers):
             st = stores[l]
-            st.evict(seqs, 1)
-            st.write(seqs, newk[l, i], newv[l, i])
+            if args.separate_write:
+                st.evict(seqs, 1)
+                st.write(seqs, newk[l, i], newv[l, i])
+            else:
+                st.decode_write(seqs, newk[l, i, :, 0], newv[l, i, :, 0])
             st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
 
     def step_bytes():
@@ -462,11 +467,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; keys/values drawn on the GPU, Philox4x32-10)",
         "config": {
-            "workload": (f"qwen3-8b-shaped decode step: {n_layers} layers x (evict 1 + append 1 + GQA decode "
-                         f"attention), {hq} q / {hkv} kv heads, head_dim 128, batch {B}, {ctx}-token context, "
+            "workload": (f"qwen3-8b-shaped decode step: {n_layers} layers x (write: evict 1 + append 1, "
+                         f"then GQA decode attention), {hq} q / {hkv} kv heads, head_dim 128, batch {B}, {ctx}-token context, "
                          "INT2 KV in 64-token pages (shuffled), BF16 sink 64 + window 256"),
             "layers": n_layers, "batch": B, "context": ctx, "q_heads": hq, "kv_heads": hkv,
             "headline_config": full,
+            "write_calls": "evict + append" if args.separate_write else "one decode-step write",
         },
         "attn_only": {"us_per_layer": round(attn_ms * 1e3, 2), "gbps": round(attn_gbps, 1),
                       "pct_peak": round(100 * attn_gbps / PEAK_GBPS, 2),

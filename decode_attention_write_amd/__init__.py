@@ -38,7 +38,8 @@ EXPORTS = [
     "oscar_calibrate_host", "oscar_calibrate_value_host", "oscar_fold_value_rotation", "oscar_kv_buffer_bytes", "oscar_kv_create", "oscar_kv_set_rotation",
     "oscar_kv_write", "oscar_kv_evict_window", "oscar_decode_workspace_bytes", "oscar_decode_attn",
     "oscar_kv_seq_info", "oscar_kv_get_page_table", "oscar_kv_free_pages", "oscar_kv_reset_seq",
-    "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel", "oscar_kv_set_decode_deterministic",
+    "oscar_kv_decode_write", "oscar_kv_set_decode_split", "oscar_kv_set_decode_kernel",
+    "oscar_kv_set_decode_deterministic",
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
 ]
@@ -86,6 +87,7 @@ def load():
         "oscar_kv_free_pages": [P, P, P],
         "oscar_kv_reset_seq": [P, I32, P],
         "oscar_kv_set_decode_split": [P, I32],
+        "oscar_kv_decode_write": [P, P, I32, P, P, P],
         "oscar_kv_set_decode_kernel": [P, I32],
         "oscar_kv_set_decode_deterministic": [P, I32],
         "oscar_kv_set_timing": [P, I32],
@@ -178,6 +180,14 @@ def oscar_kv_evict_window(store, seq_ids, n_evict, stream=None):
                                         None if store.plan_only else _stream(stream)))
 
 
+def oscar_kv_decode_write(store, seq_ids, k, v, stream=None):
+    """The decode step's write: evict when the window is full, then append one token.
+    k, v: bf16 device tensors [n_seqs, Hkv, 128] (contiguous)."""
+    ids, p = _i32(seq_ids)
+    _check(load().oscar_kv_decode_write(store.handle, p, len(ids), _ptr(k), _ptr(v),
+                                        None if store.plan_only else _stream(stream)))
+
+
 def oscar_decode_workspace_bytes(store, seq_ids):
     ids, p = _i32(seq_ids)
     n = ctypes.c_size_t(0)
@@ -251,6 +261,9 @@ class KVStore:
 
     def evict(self, seq_ids, n_evict=1, stream=None):
         oscar_kv_evict_window(self, seq_ids, n_evict, stream)
+
+    def decode_write(self, seq_ids, k, v, stream=None):
+        oscar_kv_decode_write(self, seq_ids, k, v, stream)
 
     def workspace_bytes(self, seq_ids):
         return oscar_decode_workspace_bytes(self, seq_ids)

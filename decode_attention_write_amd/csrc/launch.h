@@ -50,6 +50,27 @@ struct EvictSeq {
   int32_t n_int2;  // INT2 count before the call
 };
 
+// The decode step's write: per sequence, evict the oldest window token when the window is full,
+// then append one token.
+struct StepSeq {
+  int32_t seq;
+  int32_t len0;    // length before the call
+  int32_t n_int2;  // INT2 count before the call
+  int32_t src;     // row of this sequence in the call's k/v arrays
+  int32_t evict;   // 1: the window is full, evict its oldest token first
+};
+
+struct StepArgs {
+  const uint16_t* k;  // bf16 [n_seqs_call][hkv][128]
+  const uint16_t* v;
+  uint8_t* pool;
+  uint16_t* ring;
+  const int32_t* page_table;
+  const uint8_t* rot;
+  int32_t hkv, max_pages, n_seqs;
+  StepSeq seqs[CHUNK];
+};
+
 struct EvictArgs {
   uint8_t* pool;
   uint16_t* ring;
@@ -121,6 +142,7 @@ hipError_t launch_run(const RunArgs& a, hipStream_t s);
 hipError_t launch_write(const WriteArgs& a, int n_tiles, hipStream_t s);
 hipError_t launch_append(const WriteArgs& a, hipStream_t s);   // no INT2 tokens in the call
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
+hipError_t launch_step_write(const StepArgs& a, hipStream_t s);
 // decode attention: prepared-query + split kernels (matrix-core path) or the reference-grade
 // fp32 kernel, then the split combine
 // (t0, t1: optional events recorded on s right before and after the split kernel)

@@ -424,6 +424,76 @@ int oscar_kv_evict_window(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, 
   return OSCAR_OK;
 }
 
+int oscar_kv_decode_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
+                          void* stream) {
+  if (!kv) { set_error("oscar_kv_decode_write: null handle"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (!kv->plan_only && (!k || !v)) { set_error("oscar_kv_decode_write: null k or v"); return OSCAR_E_ARG; }
+  if (!kv->has_rotation) { set_error("oscar_kv_decode_write: rotation not set"); return OSCAR_E_STATE; }
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  int64_t need = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (kv->len[s] == 0) {
+      set_error("oscar_kv_decode_write: sequence %d is empty (its first write takes oscar_kv_write)", s);
+      return OSCAR_E_STATE;
+    }
+    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
+    if (win == kWin && kv->n_int2[s] % kPage == 0) {
+      if (kv->n_int2[s] / kPage + 1 > maxp) {
+        set_error("oscar_kv_decode_write: sequence %d exceeds max_pages_per_seq", s);
+        return OSCAR_E_NOPAGE;
+      }
+      ++need;
+    }
+  }
+  if (need > static_cast<int64_t>(kv->fifo.size())) {
+    set_error("oscar_kv_decode_write: needs %lld pages, %zu free", static_cast<long long>(need), kv->fifo.size());
+    return OSCAR_E_NOPAGE;
+  }
+  // ---- commit
+  std::vector<std::pair<int32_t, int32_t>> upd;
+  std::vector<StepSeq> plan(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
+    const bool ev = (win == kWin);
+    plan[i] = StepSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), i, ev ? 1 : 0};
+    if (ev) {
+      if (kv->n_int2[s] % kPage == 0) {
+        const int32_t page = kv->fifo.front();
+        kv->fifo.pop_front();
+        const int32_t idx = static_cast<int32_t>(s * maxp + kv->n_int2[s] / kPage);
+        kv->table[idx] = page;
+        upd.emplace_back(idx, page);
+      }
+      kv->n_int2[s] += 1;
+    }
+    kv->len[s] += 1;
+  }
+  if (kv->plan_only) return OSCAR_OK;
+  hipStream_t st = as_stream(stream);
+  rc = push_table(kv, upd, st);
+  if (rc) return rc;
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    StepArgs a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.pool = static_cast<uint8_t*>(kv->desc.pool);
+    a.ring = static_cast<uint16_t*>(kv->desc.ring);
+    a.page_table = kv->desc.page_table;
+    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+    a.hkv = kv->desc.num_kv_heads;
+    a.max_pages = kv->desc.max_pages_per_seq;
+    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
+    hipError_t e = launch_step_write(a, st);
+    if (e != hipSuccess) return hip_fail(e, "oscar_kv_decode_write: launch");
+  }
+  return OSCAR_OK;
+}
+
 int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, size_t* bytes) {
   if (!kv || !bytes) { set_error("oscar_decode_workspace_bytes: null argument"); return OSCAR_E_ARG; }
   int rc = check_seqs(kv, seq_ids, n_seqs);

@@ -238,6 +238,19 @@ int oscar_kv_write(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t
 int oscar_kv_evict_window(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t n_evict,
                           void *stream);
 
+/*
+ * The decode step's write in one launch: for each listed (non-empty) sequence,
+ * when its window holds 256 tokens, move the oldest one into INT2 (as
+ * oscar_kv_evict_window with n_evict = 1, taking a page from the FIFO when the
+ * INT2 index is a multiple of 64), then append one token (as oscar_kv_write with
+ * n_new = 1).  The stored state equals that of the two calls.  k, v: bf16 device
+ * arrays [n_seqs][num_kv_heads][128], row i for seq_ids[i].
+ * Errors: OSCAR_E_ARG, OSCAR_E_STATE (an empty sequence, or no rotation),
+ * OSCAR_E_NOPAGE; nothing is changed on error.
+ */
+int oscar_kv_decode_write(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *k,
+                          const void *v, void *stream);
+
 /* Device workspace bytes oscar_decode_attn needs for these sequences in their
  * current state (split-K partials, prepared queries, per-split page counters). */
 int oscar_decode_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs,

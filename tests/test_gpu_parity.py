@@ -234,6 +234,55 @@ def test_evict_append_decode_cycle(gpu_lib):
         assert st.seq_info(s) == (470, 470 - 320)
 
 
+def test_fused_decode_write_matches_evict_then_write(gpu_lib):
+    """The one-launch decode-step write leaves pool, ring and page table bit-identical to eviction
+    (when the window is full) followed by a one-token write, for sequences in the sink, in a filling
+    window and evicting across INT2 page boundaries; decode over the fused store matches the oracle."""
+    hkv, hq = 2, 8
+    starts = {0: 10, 1: 300, 2: 400, 3: 320 + 127}
+    ids = [3, 1, 0, 2]
+    _case("fused decode-step write vs evict + write")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 4, hkv)
+    free = synth.page_permutation(synth.CFG_QWEN3_4B, 4, 16)
+    fused = _store(gpu_lib, hq, hkv, 4, 8, 16, free, rot)
+    split = _store(gpu_lib, hq, hkv, 4, 8, 16, free, rot)
+    ora = ostore.OracleStore(hkv, 4, 8, 16, free, rot)
+    n_steps = 70
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, ids, hkv, max(starts.values()) + n_steps)
+    row = {s: b for b, s in enumerate(ids)}
+    for s, n in starts.items():
+        kb, vb = ks[row[s]:row[s] + 1, :n], vs[row[s]:row[s] + 1, :n]
+        fused.write([s], parity.to_dev_bf16(kb), parity.to_dev_bf16(vb))
+        split.write([s], parity.to_dev_bf16(kb), parity.to_dev_bf16(vb))
+        ora.write([s], kb, vb)
+    pos = dict(starts)
+    for step in range(n_steps):
+        kt = np.stack([ks[row[s], pos[s]] for s in ids])       # [n_seqs, Hkv, 128]
+        vt = np.stack([vs[row[s], pos[s]] for s in ids])
+        full = [s for s in ids if split.seq_info(s)[0] - 64 - split.seq_info(s)[1] == 256]
+        fused.decode_write(ids, parity.to_dev_bf16(kt), parity.to_dev_bf16(vt))
+        if full:
+            split.evict(full, 1)
+            ora.evict(full, 1)
+        split.write(ids, parity.to_dev_bf16(kt[:, None]), parity.to_dev_bf16(vt[:, None]))
+        ora.write(ids, kt[:, None], vt[:, None])
+        for s in ids:
+            pos[s] += 1
+        a, b = parity.export(fused), parity.export(split)
+        for x, y, name in zip(a, b, ("pool", "ring", "table")):
+            assert np.array_equal(x, y), (step, name)
+        for s in ids:
+            assert fused.seq_info(s) == split.seq_info(s) == (int(ora.length[s]), int(ora.n_int2[s]))
+    assert np.array_equal(parity.export(fused)[2], ora.page_table)
+    q = synth.decode_queries(synth.CFG_QWEN3_4B, 4, 4, hq, hkv, step=n_steps)
+    out = fused.decode(ids, parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    gpu = parity.export(fused)
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
+    assert parity.rel_l2(out, iso) <= ISO_TOL
+    ref = attention.decode_store(ora, q, ids, SCALE, hq)
+    assert parity.rel_l2(out, ref) <= E2E_TOL
+
+
 @pytest.mark.parametrize("kernel", [0, 1])
 def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
     """Outputs do not depend on the split size (beyond rounding), repeat bitwise, and do not depend

@@ -222,3 +222,58 @@ def test_binding_constants_match_header():
     assert int(consts["OSCAR_TIMING_PAIRS"]) == oscar.TIMING_PAIRS
     assert int(consts["OSCAR_TIMED_DECODE"]) == oscar.TIMED_DECODE
     assert int(consts["OSCAR_TIMED_WRITE"]) == oscar.TIMED_WRITE
+
+
+def test_plan_only_decode_write_matches_evict_then_write():
+    """The fused decode-step write keeps the same books as evict-when-full followed by a one-token
+    write: page tables, free list and lengths agree step by step, across page boundaries."""
+    free = np.random.default_rng(3).permutation(12).astype(np.int32)
+    fused, split = _plan_store(free=free), _plan_store(free=free)
+    starts = {0: 10, 1: 300, 2: 320 + 63, 3: 320 + 127}
+    for s, n in starts.items():
+        fused.write([s], None, None, n_new=n)
+        split.write([s], None, None, n_new=n)
+    ids = [3, 1, 0, 2]
+    for step in range(80):
+        fused.decode_write(ids, None, None)
+        full = [s for s in ids if split.seq_info(s)[0] - 64 - split.seq_info(s)[1] == 256]
+        if full:
+            split.evict(full, 1)
+        split.write(ids, None, None, n_new=1)
+        assert np.array_equal(fused.page_table(), split.page_table()), step
+        assert list(fused.free_pages()) == list(split.free_pages()), step
+        for s in ids:
+            assert fused.seq_info(s) == split.seq_info(s), (step, s)
+    assert fused.seq_info(3) == (320 + 127 + 80, 127 + 80)
+    assert fused.seq_info(1) == (380, 60)
+
+
+def test_decode_write_errors_leave_state_unchanged():
+    s = _plan_store(num_pages=4, max_pages=2)
+    s.write([0], None, None, n_new=320 + 128)      # 2 pages = max_pages_per_seq, INT2 full
+    s.write([1], None, None, n_new=320 + 64)       # 1 page
+    snap = (s.page_table().copy(), list(s.free_pages()), s.seq_info(0), s.seq_info(1))
+
+    def unchanged():
+        assert np.array_equal(s.page_table(), snap[0]) and list(s.free_pages()) == snap[1]
+        assert (s.seq_info(0), s.seq_info(1)) == snap[2:]
+
+    cases = [
+        (lambda: s.decode_write([2], None, None), oscar.E_STATE),        # empty sequence
+        (lambda: s.decode_write([1, 2], None, None), oscar.E_STATE),
+        (lambda: s.decode_write([0], None, None), oscar.E_NOPAGE),       # > max_pages_per_seq
+        (lambda: s.decode_write([1, 1], None, None), oscar.E_ARG),
+        (lambda: s.decode_write([7], None, None), oscar.E_ARG),
+    ]
+    for fn, status in cases:
+        with pytest.raises(oscar.OscarError) as e:
+            fn()
+        assert e.value.status == status
+        unchanged()
+    s.decode_write([1], None, None)                # takes the last free page
+    assert s.seq_info(1) == (320 + 65, 65) and list(s.free_pages()) == []
+    for _ in range(63):
+        s.decode_write([1], None, None)            # fills that page
+    with pytest.raises(oscar.OscarError) as e:
+        s.decode_write([1], None, None)            # needs a page, none free
+    assert e.value.status == oscar.E_NOPAGE
