@@ -95,30 +95,52 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
 
   const size_t row = static_cast<size_t>(a.hkv) * D;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
-  for (int tile = tile0; tile < tile1; ++tile) {
-    const int n_here = min(PAGE, a.n_new - tile * PAGE);
-    const int p0 = sq.len0 + tile * PAGE;
-    const uint16_t* ksrc = a.k + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
-    const uint16_t* vsrc = a.v + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(tile) * PAGE) * row + kvh * D;
-    // page of this tile (INT2 tiles only), fetched before the tile's work
-    const int page = (n_int2 > 0 && p0 >= SINK) ? a.page_table[static_cast<size_t>(sq.seq) * a.max_pages + (tile - 1)] : 0;
-    // a 64 x 128 bf16 tile (keys, later values) into LDS, 16 bytes per thread and step; rows past
-    // the call's tokens are zero
-    auto load_tile = [&](const uint16_t* src) {
-      v4u_w w[4];
+  // A 64 x 128 bf16 tile (keys or values) moves global -> registers (16 bytes per thread and
+  // step) -> LDS.  The loads of the next tile are issued as soon as the registers have been
+  // stored, so they are in flight while this tile is rotated and quantized.  Loads are never
+  // conditional (rows past the call's tokens re-read the last row and are zeroed when stored;
+  // past the work-group's last tile the last tile is read again), which keeps the compiler's
+  // wait on them a counted one instead of a full drain.
+  auto issue = [&](const uint16_t* base, int t, v4u_w* w) {
+    const int nh = min(PAGE, a.n_new - t * PAGE);
+    const uint16_t* src = base + (static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(t) * PAGE) * row + kvh * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = tid + 256 * r, j = i >> 4, c8 = i & 15;
-        w[r] = v4u_w{0u, 0u, 0u, 0u};
-        if (j < n_here) w[r] = *reinterpret_cast<const v4u_w*>(src + static_cast<size_t>(j) * row + 8 * c8);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r, j = min(i >> 4, nh - 1), c8 = i & 15;
+      w[r] = *reinterpret_cast<const v4u_w*>(src + static_cast<size_t>(j) * row + 8 * c8);
+    }
+  };
+  // Register -> LDS.  The rows past the call's tokens are then overwritten with zeros (LDS stores
+  // only: selecting in registers let the compiler hoist the select, and with it the wait on the
+  // loads, above the rotation).
+  auto stash = [&](int nh, const v4u_w* w) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r;
+      *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = w[r];
+    }
+    if (nh < PAGE) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = tid + 256 * r;
-        *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = w[r];
+        if ((i >> 4) >= nh) *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = v4u_w{0u, 0u, 0u, 0u};
       }
-    };
-    load_tile(ksrc);
+    }
+  };
+  // page ids through the scalar cache (the table is not written by this kernel)
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(sq.seq) * a.max_pages);
+  v4u_w kreg[4], vreg[4];
+  issue(a.k, tile0, kreg);
+  issue(a.v, tile0, vreg);
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int n_here = min(PAGE, a.n_new - tile * PAGE);
+    const int p0 = sq.len0 + tile * PAGE;
+    const int next = min(tile + 1, tile1 - 1);
+    // page of this tile (INT2 tiles only), fetched before the tile's work
+    const int page = (n_int2 > 0 && p0 >= SINK) ? ptab[tile - 1] : 0;
+    stash(n_here, kreg);
+    issue(a.k, next, kreg);
     __syncthreads();
 
     // rotation: 16-token column tiles; each (output tile, K-step) takes the two R^T terms
@@ -138,19 +160,32 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       }
     }
     __syncthreads();
-    load_tile(vsrc);
+    stash(n_here, vreg);
+    issue(a.v, next, vreg);
     __syncthreads();
 
     // BF16 destinations: sink / window (tiles holding such positions only)
     const bool any_bf16 = (p0 < SINK) || (p0 + n_here > SINK + n_int2);
     if (any_bf16) {
-      for (int i = tid; i < n_here * D; i += 256) {
-        const int j = i / D, c = i % D, p = p0 + j;
+      // 8 channels of one token per thread and step, a fixed number of steps (a loop of unknown
+      // trip count around the stores would make every later wait on the prefetch a full drain)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = tid + 256 * r, j = i >> 4, c8 = 8 * (i & 15), p = p0 + j;
         const bool int2 = (p >= SINK) && (p < SINK + n_int2);
-        if (int2) continue;
-        const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
-        a.ring[ring_head + static_cast<size_t>(slot) * D + c] = f32_to_bf16(x[j][c]);
-        a.ring[ring_head + static_cast<size_t>(RING + slot) * D + c] = tin[j][c];
+        if (j < n_here && !int2) {
+          const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
+          const v4f_w x0 = *reinterpret_cast<const v4f_w*>(&x[j][c8]);
+          const v4f_w x1 = *reinterpret_cast<const v4f_w*>(&x[j][c8 + 4]);
+          const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          v4u_w kw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            kw[e] = static_cast<uint32_t>(f32_to_bf16(xs[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(xs[2 * e + 1])) << 16);
+          *reinterpret_cast<v4u_w*>(a.ring + ring_head + static_cast<size_t>(slot) * D + c8) = kw;
+          *reinterpret_cast<v4u_w*>(a.ring + ring_head + static_cast<size_t>(RING + slot) * D + c8) =
+              *reinterpret_cast<const v4u_w*>(&tin[j][c8]);
+        }
       }
     }
 
