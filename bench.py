@@ -230,6 +230,85 @@ def prefill_leg(reps=5):
     return res
 
 
+def layer_leg(cfg, hq, hkv, lengths, reps, label):
+    """One attention layer over sequences of the given lengths (one R_K per KV head, pages in a
+    seeded shuffled order): prefill writes, then `reps` decode steps (the decode-step write of
+    one token per sequence, then decode attention), each after one untimed step.  Returns the
+    split kernel's mean launch time (library events), the whole step's time and their rates."""
+    import numpy as np
+    import torch
+
+    import decode_attention_write_amd as oscar
+    import synth
+    from synth import gpu as sgpu
+
+    B = len(lengths)
+    rots = np.stack([oscar.oscar_calibrate_host(synth.bf16_bits_to_f32(synth.calibration_queries(cfg, 0, h)))[0]
+                     for h in range(hkv)])
+    max_pages = -(-(max(lengths) + reps + 2) // 64) + 1
+    num_pages = sum(-(-(L + reps + 2) // 64) for L in lengths) + B
+    st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, 0, num_pages))
+    st.set_rotation(rots)
+    prm = sgpu.HeadParams(cfg, 0, hkv)
+    n_new = reps + 1
+    kbuf = torch.empty((1, max(lengths) + n_new, hkv, 128), dtype=torch.int16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    newk = torch.empty((n_new, B, hkv, 128), dtype=torch.int16, device="cuda")
+    newv = torch.empty_like(newk)
+    for s, L in enumerate(lengths):
+        sgpu.draw_kv(prm, s, 0, L + n_new, kbuf[0, :L + n_new], vbuf[0, :L + n_new])
+        st.write([s], kbuf[:, :L], vbuf[:, :L])
+        newk[:, s] = kbuf[0, L:L + n_new]
+        newv[:, s] = vbuf[0, L:L + n_new]
+    del kbuf, vbuf
+    seqs = list(range(B))
+    q = torch.from_numpy(synth.decode_queries(cfg, 0, B, hq, hkv).view(np.int16)).cuda()
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(st.workspace_bytes(seqs) // 4 + (1 << 18), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+
+    def step(i):
+        st.decode_write(seqs, newk[i], newv[i])
+        st.decode(seqs, q, scale, out=out, ws=ws)
+
+    # the layer's cache may fit the 256 MB last-level cache: overwrite a larger buffer before
+    # every timed step so that each one reads its pages from HBM
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+    st.set_timing(True)
+    step(0)
+    torch.cuda.synchronize()
+    st.read_timing(oscar.TIMED_DECODE)
+    info = [st.seq_info(s) for s in seqs]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(i)
+        evs[i][0].record()
+        step(1 + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    n, k_ms, each = st.read_timing(oscar.TIMED_DECODE, each=True)
+    st.set_timing(False)
+    assert n == reps * -(-B // 64), n
+    step_us = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+    kbytes = float(np.mean([split_kernel_bytes([L + i + 1 for L, _ in info], [n2 + i + 1 for _, n2 in info], hkv)
+                            for i in range(reps)]))
+    kernel_us = k_ms * 1e3 / n
+    res = {
+        "workload": label,
+        "split_kernel_us": round(kernel_us, 2),
+        "split_kernel_us_median": round(float(np.median(each)) * 1e3, 2),
+        "split_kernel_bytes": int(kbytes),
+        "split_kernel_gbps": round(kbytes / kernel_us / 1e3, 1),
+        "split_kernel_pct_peak": round(100 * kbytes / kernel_us / 1e3 / PEAK_GBPS, 2),
+        "step_us_median": round(float(np.median(step_us)), 2),
+        "steps": reps,
+    }
+    log(f"{label}: split kernel {res['split_kernel_us']} us = {res['split_kernel_gbps']} GB/s "
+        f"({res['split_kernel_pct_peak']}% of 8 TB/s); step (write + attention) {res['step_us_median']} us")
+    del st, newk, newv, ws, flush
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +323,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 131072-token prefill-write leg")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the single-layer legs (32K x 8 GQA 4; ragged 8K-128K x 16 GQA 8)")
     ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
     ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
     ap.add_argument("--deterministic", action="store_true",
@@ -270,7 +351,8 @@ def main():
     cfg = synth.CFG_QWEN3_8B
     n_layers, B, ctx = args.layers, args.batch, args.context
     hq, hkv = 32, 8
-    n_steps_total = args.warmup + 2 * args.steps  # warmup, the timed steps, the kernel-timed steps
+    # warmup, the timed steps, then warmup and the kernel-timed steps again
+    n_steps_total = 2 * args.warmup + 2 * args.steps
     max_pages = -(-(ctx + n_steps_total + 64) // 64)
     num_pages = B * max_pages
     full = (n_layers, B, ctx) == (36, 32, 100000)
@@ -374,15 +456,22 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms/step), {step_gbps:.0f} GB/s")
 
     # ---- the same decode steps again, with the library's fence-free HIP events around every
-    # split-kernel launch (on the launch stream): the roofline's kernel durations
-    info0 = [[st.seq_info(s) for s in seqs] for st in stores]
+    # split-kernel launch (on the launch stream): the roofline's kernel durations.  Like the
+    # block above it starts with untimed warmup steps, here with the events already in use
+    # (without them the block's first step measured ~15 % slower launches)
     for st in stores:
         st.set_timing(True)
+    for i in range(args.warmup):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    for st in stores:
+        st.read_timing(oscar.TIMED_DECODE)      # discards the warmup launches
+    info0 = [[st.seq_info(s) for s in seqs] for st in stores]
     kt0, kt1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     kt0.record()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+        step(2 * args.warmup + args.steps + i)
     kt1.record()
     torch.cuda.synchronize()
     ms_per_step_kt = kt0.elapsed_time(kt1) / args.steps
@@ -499,6 +588,13 @@ def main():
     }
     if not args.no_prefill:
         result["prefill"] = prefill_leg()
+    if not args.no_layers:
+        result["layer_qwen3_4b_32k_b8"] = layer_leg(
+            synth.CFG_QWEN3_4B, 32, 8, [32768] * 8, 20,
+            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context")
+        result["layer_qwen3_32b_ragged_b16"] = layer_leg(
+            synth.CFG_QWEN3_32B, 64, 8, [int(x) for x in synth.ragged_lengths(synth.CFG_QWEN3_32B, 16, 8192, 131072)],
+            20, "qwen3-32b-shaped layer: 64 q / 8 kv heads (GQA 8), batch 16, lengths U[8192, 131072]")
     if args.copy_calib_mib:
         # a plain copy of known size, for scaling the memory counters of a profiled run
         n = args.copy_calib_mib * (1 << 20) // 4

@@ -89,8 +89,7 @@ def test_qwen3_4b_full_context(gpu_lib):
     seqs = list(range(B))
     st.write(seqs, kbuf[:, :L].contiguous(), vbuf[:, :L].contiguous())
     before = parity.export(st)
-    st.evict(seqs, 1)
-    st.write(seqs, kbuf[:, L:].contiguous(), vbuf[:, L:].contiguous())
+    st.decode_write(seqs, kbuf[:, L].contiguous(), vbuf[:, L].contiguous())   # evicts, then appends
     gpu = parity.export(st)
     # allocator: one call, sequences in order, FIFO identity
     ora_t = ostore.OracleStore(1, B, max_pages, num_pages, range(num_pages), np.eye(D, dtype=np.float32)[None])
@@ -121,7 +120,7 @@ def test_qwen3_4b_full_context(gpu_lib):
 
 
 def test_prefill_131072_then_1024_appends(gpu_lib):
-    """One 131072-token sequence x 8 KV heads, then 1024 single-token evict + append steps."""
+    """One 131072-token sequence x 8 KV heads, then 1024 decode-step writes (evict 1 + append 1 each)."""
     import torch
     from synth import gpu as sg
     cfg, hkv, hq, L, n_app = synth.CFG_PREFILL, 8, 32, 131072, 1024
@@ -147,8 +146,7 @@ def test_prefill_131072_then_1024_appends(gpu_lib):
     for i in range(n_app):
         if i == n_app - 1:
             ring_before = parity.export(st)[1]
-        st.evict([0], 1)
-        st.write([0], kbuf[:, L + i:L + i + 1].contiguous(), vbuf[:, L + i:L + i + 1].contiguous())
+        st.decode_write([0], kbuf[:, L + i].contiguous(), vbuf[:, L + i].contiguous())
     gpu = parity.export(st)
     assert st.seq_info(0) == (L + n_app, L + n_app - 320)
     n_pages_now = -(-(L + n_app - 320) // 64)

@@ -53,7 +53,8 @@ def _page_loops(lines, symbol):
     end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
     blocks, cur = [], None
     for ln in lines[start:end]:
-        if re.match(r"^\.LBB\d+_\d+:", ln):
+        # named (.LBB) and unnamed (; %bb.N) basic blocks each start a block
+        if re.match(r"^\.LBB\d+_\d+:", ln) or re.match(r"^; %bb\.\d+:", ln):
             cur = [ln]
             blocks.append(cur)
         elif cur is not None:
