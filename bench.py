@@ -268,8 +268,7 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label):
     scale = 1.0 / math.sqrt(128)
 
     def step(i):
-        st.decode_write(seqs, newk[i], newv[i])
-        st.decode(seqs, q, scale, out=out, ws=ws)
+        st.decode_step(seqs, newk[i], newv[i], q, scale, out=out, ws=ws)
 
     # the layer's cache may fit the 256 MB last-level cache: overwrite a larger buffer before
     # every timed step so that each one reads its pages from HBM
@@ -330,6 +329,8 @@ def main():
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed page range per split (no page sharing between the splits of a unit)")
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
+    ap.add_argument("--two-call", action="store_true",
+                    help="development: the decode-step write and the attention as two calls")
     ap.add_argument("--separate-write", action="store_true",
                     help="write each step with the eviction and the append as two calls (comparison)")
     args = ap.parse_args()
@@ -421,9 +422,12 @@ def main():
             if args.separate_write:
                 st.evict(seqs, 1)
                 st.write(seqs, newk[l, i], newv[l, i])
-            else:
+                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+            elif args.two_call:
                 st.decode_write(seqs, newk[l, i, :, 0], newv[l, i, :, 0])
-            st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+            else:
+                st.decode_step(seqs, newk[l, i, :, 0], newv[l, i, :, 0], qs[l], scale, out=outs[l], ws=ws)
 
     def step_bytes():
         tot = 0
@@ -561,7 +565,9 @@ def main():
                          "INT2 KV in 64-token pages (shuffled), BF16 sink 64 + window 256"),
             "layers": n_layers, "batch": B, "context": ctx, "q_heads": hq, "kv_heads": hkv,
             "headline_config": full,
-            "write_calls": "evict + append" if args.separate_write else "one decode-step write",
+            "write_calls": ("evict + append, then attention" if args.separate_write else
+                            "decode-step write, then attention" if args.two_call else
+                            "one decode-step call (write + attention)"),
         },
         "attn_only": {"us_per_layer": round(attn_ms * 1e3, 2), "gbps": round(attn_gbps, 1),
                       "pct_peak": round(100 * attn_gbps / PEAK_GBPS, 2),

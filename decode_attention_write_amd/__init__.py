@@ -42,6 +42,7 @@ EXPORTS = [
     "oscar_kv_set_decode_deterministic",
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
+    "oscar_decode_step_workspace_bytes", "oscar_decode_step",
 ]
 
 
@@ -92,6 +93,8 @@ def load():
         "oscar_kv_set_decode_deterministic": [P, I32],
         "oscar_kv_set_timing": [P, I32],
         "oscar_kv_read_timing": [P, I32, P, P, P],
+        "oscar_decode_step_workspace_bytes": [P, P, I32, P],
+        "oscar_decode_step": [P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -203,6 +206,22 @@ def oscar_decode_attn(store, seq_ids, q, sm_scale, out, ws, stream=None):
                                     _ptr(ws), nbytes, None if store.plan_only else _stream(stream)))
 
 
+def oscar_decode_step_workspace_bytes(store, seq_ids):
+    ids, p = _i32(seq_ids)
+    n = ctypes.c_size_t(0)
+    _check(load().oscar_decode_step_workspace_bytes(store.handle, p, len(ids), ctypes.byref(n)))
+    return n.value
+
+
+def oscar_decode_step(store, seq_ids, k, v, q, sm_scale, out, ws, stream=None):
+    """One whole decode step (the decode-step write of k, v, then attention of q over everything
+    stored).  k, v: bf16 [n_seqs, Hkv, 128]; q: bf16 [n_seqs, Hq, 128]; out: fp32 [n_seqs, Hq, 128]."""
+    ids, p = _i32(seq_ids)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().oscar_decode_step(store.handle, p, len(ids), _ptr(k), _ptr(v), _ptr(q), ctypes.c_float(sm_scale),
+                                    _ptr(out), _ptr(ws), nbytes, None if store.plan_only else _stream(stream)))
+
+
 # ---------------------------------------------------------------------------- store object
 
 class KVStore:
@@ -276,6 +295,20 @@ class KVStore:
         if ws is None:
             ws = torch.empty(max(4, self.workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)
         oscar_decode_attn(self, seq_ids, q, sm_scale, out, ws, stream)
+        return out
+
+    def step_workspace_bytes(self, seq_ids):
+        return oscar_decode_step_workspace_bytes(self, seq_ids)
+
+    def decode_step(self, seq_ids, k, v, q, sm_scale, out=None, ws=None, stream=None):
+        """The decode-step write and the decode attention in one call; returns out."""
+        if out is None and not self.plan_only:
+            import torch
+            out = torch.empty((len(seq_ids), self.hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+        if ws is None and not self.plan_only:
+            import torch
+            ws = torch.empty(max(4, self.step_workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)
+        oscar_decode_step(self, seq_ids, k, v, q, sm_scale, out, ws, stream)
         return out
 
     def seq_info(self, seq):

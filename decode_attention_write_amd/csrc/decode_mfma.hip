@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "step_write.h"
 
 namespace oscar {
 
@@ -70,10 +71,10 @@ __host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
 }
 
 // ------------------------------------------------------------------ query preparation
-// Grid (KV heads, sequences of the chunk), 256 threads.
+// One (KV head, sequence of the chunk) per 256-thread work-group.
 template <int G>
-__global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
-  const int kvh = blockIdx.x, sl = blockIdx.y, tid = threadIdx.x;
+__device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl) {
+  const int tid = threadIdx.x;
   const DecodeSeq sq = a.seqs[sl];
   __shared__ float qf[G][D];
   __shared__ float sig[G];
@@ -155,6 +156,19 @@ __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) {
     }
     wa[idx] = v;
   }
+}
+
+// Grid (KV heads, sequences of the chunk), 256 threads.
+template <int G>
+__global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) { qprep_block<G>(a, blockIdx.x, blockIdx.y); }
+
+// The decode step's write and the query preparation in one launch: both work per (KV head,
+// sequence) and read that head's R_K.  The write lands in the ring before the split kernel,
+// which runs after this launch on the same stream, reads it (the new token attends to itself).
+template <int G>
+__global__ __launch_bounds__(256) void k_step_qprep(StepArgs w, DecodeArgs a) {
+  step_write_block(w, blockIdx.x, blockIdx.y);
+  qprep_block<G>(a, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -739,8 +753,9 @@ int decode_resident_workgroups(int gqa, int kernel) {
 }
 
 template <int G>
-static hipError_t launch_g(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+static hipError_t launch_g(const StepArgs* w, const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (w) hipLaunchKernelGGL(k_step_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, *w, a);
+  else hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
   if (t0) {
     const hipError_t e = hipEventRecord(t0, s);
     if (e != hipSuccess) return e;
@@ -753,12 +768,13 @@ static hipError_t launch_g(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hi
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_decode_mfma(const StepArgs* w, const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (w && (w->n_seqs != a.n_seqs || w->hkv != a.hkv)) return hipErrorInvalidValue;
   switch (a.hq / a.hkv) {
-    case 1: return launch_g<1>(a, s, t0, t1);
-    case 2: return launch_g<2>(a, s, t0, t1);
-    case 4: return launch_g<4>(a, s, t0, t1);
-    case 8: return launch_g<8>(a, s, t0, t1);
+    case 1: return launch_g<1>(w, a, s, t0, t1);
+    case 2: return launch_g<2>(w, a, s, t0, t1);
+    case 4: return launch_g<4>(w, a, s, t0, t1);
+    case 8: return launch_g<8>(w, a, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

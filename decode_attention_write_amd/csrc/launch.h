@@ -146,7 +146,9 @@ hipError_t launch_step_write(const StepArgs& a, hipStream_t s);
 // decode attention: prepared-query + split kernels (matrix-core path) or the reference-grade
 // fp32 kernel, then the split combine
 // (t0, t1: optional events recorded on s right before and after the split kernel)
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
+// w (may be null): the decode step's write of the same sequences, run in the query preparation's
+// launch (k_step_qprep) instead of a launch of its own
+hipError_t launch_decode_mfma(const StepArgs* w, const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_decode_simple(const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // work-groups of the decode split kernel to plan per residency round on the current device

@@ -183,6 +183,143 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
   return best;
 }
 
+// ---- decode-step write and decode attention, shared by the one-call and two-call forms
+
+// Validation of a decode-step write (nothing is changed).
+int check_step_write(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
+                     const char* who) {
+  if (!kv) { set_error("%s: null handle", who); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (!kv->plan_only && (!k || !v)) { set_error("%s: null k or v", who); return OSCAR_E_ARG; }
+  if (!kv->has_rotation) { set_error("%s: rotation not set", who); return OSCAR_E_STATE; }
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  int64_t need = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (kv->len[s] == 0) {
+      set_error("%s: sequence %d is empty (its first write takes oscar_kv_write)", who, s);
+      return OSCAR_E_STATE;
+    }
+    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
+    if (win == kWin && kv->n_int2[s] % kPage == 0) {
+      if (kv->n_int2[s] / kPage + 1 > maxp) {
+        set_error("%s: sequence %d exceeds max_pages_per_seq", who, s);
+        return OSCAR_E_NOPAGE;
+      }
+      ++need;
+    }
+  }
+  if (need > static_cast<int64_t>(kv->fifo.size())) {
+    set_error("%s: needs %lld pages, %zu free", who, static_cast<long long>(need), kv->fifo.size());
+    return OSCAR_E_NOPAGE;
+  }
+  return OSCAR_OK;
+}
+
+// Host state of a validated decode-step write: evict where the window is full (a page from the
+// FIFO when the INT2 index is a multiple of 64), then one more token per sequence.
+std::vector<StepSeq> commit_step_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs,
+                                       std::vector<std::pair<int32_t, int32_t>>& upd) {
+  const int64_t maxp = kv->desc.max_pages_per_seq;
+  std::vector<StepSeq> plan(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
+    const bool ev = (win == kWin);
+    plan[i] = StepSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), i, ev ? 1 : 0};
+    if (ev) {
+      if (kv->n_int2[s] % kPage == 0) {
+        const int32_t page = kv->fifo.front();
+        kv->fifo.pop_front();
+        const int32_t idx = static_cast<int32_t>(s * maxp + kv->n_int2[s] / kPage);
+        kv->table[idx] = page;
+        upd.emplace_back(idx, page);
+      }
+      kv->n_int2[s] += 1;
+    }
+    kv->len[s] += 1;
+  }
+  return plan;
+}
+
+StepArgs step_args(const oscar_kv* kv, const void* k, const void* v, const std::vector<StepSeq>& plan, int c0, int n) {
+  StepArgs a{};
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.pool = static_cast<uint8_t*>(kv->desc.pool);
+  a.ring = static_cast<uint16_t*>(kv->desc.ring);
+  a.page_table = kv->desc.page_table;
+  a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+  a.hkv = kv->desc.num_kv_heads;
+  a.max_pages = kv->desc.max_pages_per_seq;
+  a.n_seqs = n;
+  for (int i = 0; i < n; ++i) a.seqs[i] = plan[c0 + i];
+  return a;
+}
+
+// Validation of a decode-attention call apart from its workspace size (nothing is changed).
+int check_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* q, float sm_scale,
+                 const float* out, const void* ws, const char* who) {
+  if (!kv) { set_error("%s: null handle", who); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  if (!kv->plan_only && (!q || !out || !ws)) { set_error("%s: null q, out or workspace", who); return OSCAR_E_ARG; }
+  if (!std::isfinite(sm_scale)) { set_error("%s: non-finite sm_scale", who); return OSCAR_E_ARG; }
+  if (!kv->has_rotation) { set_error("%s: rotation not set", who); return OSCAR_E_STATE; }
+  for (int i = 0; i < n_seqs; ++i)
+    if (kv->len[seq_ids[i]] == 0) { set_error("%s: sequence %d is empty", who, seq_ids[i]); return OSCAR_E_STATE; }
+  return OSCAR_OK;
+}
+
+// Decode attention launches over the current host state, chunk by chunk.  With a step plan (the
+// sequences' decode-step write, already committed to the host state) the write runs in the
+// query preparation's launch.
+int launch_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const std::vector<StepSeq>* plan,
+                  const void* q, float sm_scale, float* out, void* ws, hipStream_t st, const char* who,
+                  const void* k = nullptr, const void* v = nullptr) {
+  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
+  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.pool = static_cast<const uint8_t*>(kv->desc.pool);
+    a.ring = static_cast<const uint16_t*>(kv->desc.ring);
+    a.page_table = kv->desc.page_table;
+    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+    a.part = static_cast<float*>(ws);
+    a.out = out;
+    a.hkv = kv->desc.num_kv_heads;
+    a.hq = kv->desc.num_q_heads;
+    a.max_pages = kv->desc.max_pages_per_seq;
+    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    a.pages_per_split = static_cast<int32_t>(pps);
+    int64_t max_split = 1;
+    for (int i = 0; i < a.n_seqs; ++i) {
+      const int s = seq_ids[c0 + i];
+      a.seqs[i] = DecodeSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), c0 + i};
+      max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]),
+                                                            static_cast<int>(pps), kv->decode_kernel));
+    }
+    a.n_split_max = static_cast<int32_t>(max_split);
+    a.kernel = kv->decode_kernel;
+    a.share = kv->deterministic ? 0 : 1;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
+    hipError_t e;
+    if (kv->decode_kernel == 1) {
+      e = launch_decode_simple(a, st, t0, t1);
+    } else if (plan) {
+      const StepArgs w = step_args(kv, k, v, *plan, c0, a.n_seqs);
+      e = launch_decode_mfma(&w, a, st, t0, t1);
+    } else {
+      e = launch_decode_mfma(nullptr, a, st, t0, t1);
+    }
+    if (e == hipSuccess) e = launch_combine(a, st);
+    if (e != hipSuccess) return hip_fail(e, who);
+  }
+  return OSCAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,68 +563,16 @@ int oscar_kv_evict_window(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, 
 
 int oscar_kv_decode_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
                           void* stream) {
-  if (!kv) { set_error("oscar_kv_decode_write: null handle"); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_step_write(kv, seq_ids, n_seqs, k, v, "oscar_kv_decode_write");
   if (rc) return rc;
-  if (!kv->plan_only && (!k || !v)) { set_error("oscar_kv_decode_write: null k or v"); return OSCAR_E_ARG; }
-  if (!kv->has_rotation) { set_error("oscar_kv_decode_write: rotation not set"); return OSCAR_E_STATE; }
-  const int64_t maxp = kv->desc.max_pages_per_seq;
-  int64_t need = 0;
-  for (int i = 0; i < n_seqs; ++i) {
-    const int s = seq_ids[i];
-    if (kv->len[s] == 0) {
-      set_error("oscar_kv_decode_write: sequence %d is empty (its first write takes oscar_kv_write)", s);
-      return OSCAR_E_STATE;
-    }
-    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
-    if (win == kWin && kv->n_int2[s] % kPage == 0) {
-      if (kv->n_int2[s] / kPage + 1 > maxp) {
-        set_error("oscar_kv_decode_write: sequence %d exceeds max_pages_per_seq", s);
-        return OSCAR_E_NOPAGE;
-      }
-      ++need;
-    }
-  }
-  if (need > static_cast<int64_t>(kv->fifo.size())) {
-    set_error("oscar_kv_decode_write: needs %lld pages, %zu free", static_cast<long long>(need), kv->fifo.size());
-    return OSCAR_E_NOPAGE;
-  }
-  // ---- commit
   std::vector<std::pair<int32_t, int32_t>> upd;
-  std::vector<StepSeq> plan(n_seqs);
-  for (int i = 0; i < n_seqs; ++i) {
-    const int s = seq_ids[i];
-    const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
-    const bool ev = (win == kWin);
-    plan[i] = StepSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), i, ev ? 1 : 0};
-    if (ev) {
-      if (kv->n_int2[s] % kPage == 0) {
-        const int32_t page = kv->fifo.front();
-        kv->fifo.pop_front();
-        const int32_t idx = static_cast<int32_t>(s * maxp + kv->n_int2[s] / kPage);
-        kv->table[idx] = page;
-        upd.emplace_back(idx, page);
-      }
-      kv->n_int2[s] += 1;
-    }
-    kv->len[s] += 1;
-  }
+  std::vector<StepSeq> plan = commit_step_write(kv, seq_ids, n_seqs, upd);
   if (kv->plan_only) return OSCAR_OK;
   hipStream_t st = as_stream(stream);
   rc = push_table(kv, upd, st);
   if (rc) return rc;
   for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
-    StepArgs a{};
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.pool = static_cast<uint8_t*>(kv->desc.pool);
-    a.ring = static_cast<uint16_t*>(kv->desc.ring);
-    a.page_table = kv->desc.page_table;
-    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
-    a.hkv = kv->desc.num_kv_heads;
-    a.max_pages = kv->desc.max_pages_per_seq;
-    a.n_seqs = std::min(CHUNK, n_seqs - c0);
-    for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
+    const StepArgs a = step_args(kv, k, v, plan, c0, std::min(CHUNK, n_seqs - c0));
     hipError_t e = launch_step_write(a, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_kv_decode_write: launch");
   }
@@ -515,14 +600,8 @@ int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int
 
 int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* q, float sm_scale,
                       float* out, void* ws, size_t ws_bytes, void* stream) {
-  if (!kv) { set_error("oscar_decode_attn: null handle"); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_decode(kv, seq_ids, n_seqs, q, sm_scale, out, ws, "oscar_decode_attn");
   if (rc) return rc;
-  if (!kv->plan_only && (!q || !out || !ws)) { set_error("oscar_decode_attn: null q, out or workspace"); return OSCAR_E_ARG; }
-  if (!std::isfinite(sm_scale)) { set_error("oscar_decode_attn: non-finite sm_scale"); return OSCAR_E_ARG; }
-  if (!kv->has_rotation) { set_error("oscar_decode_attn: rotation not set"); return OSCAR_E_STATE; }
-  for (int i = 0; i < n_seqs; ++i)
-    if (kv->len[seq_ids[i]] == 0) { set_error("oscar_decode_attn: sequence %d is empty", seq_ids[i]); return OSCAR_E_STATE; }
   size_t need = 0;
   rc = oscar_decode_workspace_bytes(kv, seq_ids, n_seqs, &need);
   if (rc) return rc;
@@ -531,39 +610,62 @@ int oscar_decode_attn(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs
     return OSCAR_E_WORKSPACE;
   }
   if (kv->plan_only) return OSCAR_OK;
-  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
-  hipStream_t st = as_stream(stream);
-  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
-    DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.pool = static_cast<const uint8_t*>(kv->desc.pool);
-    a.ring = static_cast<const uint16_t*>(kv->desc.ring);
-    a.page_table = kv->desc.page_table;
-    a.rot = static_cast<const uint8_t*>(kv->desc.rot);
-    a.part = static_cast<float*>(ws);
-    a.out = out;
-    a.hkv = kv->desc.num_kv_heads;
-    a.hq = kv->desc.num_q_heads;
-    a.max_pages = kv->desc.max_pages_per_seq;
-    a.n_seqs = std::min(CHUNK, n_seqs - c0);
-    a.pages_per_split = static_cast<int32_t>(pps);
-    int64_t max_split = 1;
-    for (int i = 0; i < a.n_seqs; ++i) {
-      const int s = seq_ids[c0 + i];
-      a.seqs[i] = DecodeSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), c0 + i};
-      max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]),
-                                                            static_cast<int>(pps), kv->decode_kernel));
-    }
-    a.n_split_max = static_cast<int32_t>(max_split);
-    a.kernel = kv->decode_kernel;
-    a.share = kv->deterministic ? 0 : 1;
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
-    const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
-    hipError_t e = (kv->decode_kernel == 1) ? launch_decode_simple(a, st, t0, t1) : launch_decode_mfma(a, st, t0, t1);
-    if (e == hipSuccess) e = launch_combine(a, st);
-    if (e != hipSuccess) return hip_fail(e, "oscar_decode_attn: launch");
+  return launch_decode(kv, seq_ids, n_seqs, nullptr, q, sm_scale, out, ws, as_stream(stream), "oscar_decode_attn");
+}
+
+int oscar_decode_step_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, size_t* bytes) {
+  if (!kv || !bytes) { set_error("oscar_decode_step_workspace_bytes: null argument"); return OSCAR_E_ARG; }
+  int rc = check_seqs(kv, seq_ids, n_seqs);
+  if (rc) return rc;
+  // the attention runs on the state after the step's write: one more token per sequence, and
+  // one more INT2 token where the window is full.  The host mirror is advanced for the count and
+  // restored (a handle is used by one host thread at a time).
+  oscar_kv* m = const_cast<oscar_kv*>(kv);
+  std::vector<std::pair<int64_t, int64_t>> saved(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    saved[i] = {m->len[s], m->n_int2[s]};
+    if (m->len[s] > 0 && std::max<int64_t>(0, m->len[s] - kSink - m->n_int2[s]) == kWin) m->n_int2[s] += 1;
+    m->len[s] += 1;
   }
-  return OSCAR_OK;
+  rc = oscar_decode_workspace_bytes(kv, seq_ids, n_seqs, bytes);
+  for (int i = n_seqs - 1; i >= 0; --i) {
+    m->len[seq_ids[i]] = saved[i].first;
+    m->n_int2[seq_ids[i]] = saved[i].second;
+  }
+  return rc;
+}
+
+int oscar_decode_step(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
+                      const void* q, float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_step_write(kv, seq_ids, n_seqs, k, v, "oscar_decode_step");
+  if (rc) return rc;
+  rc = check_decode(kv, seq_ids, n_seqs, q, sm_scale, out, ws, "oscar_decode_step");
+  if (rc) return rc;
+  size_t need = 0;
+  rc = oscar_decode_step_workspace_bytes(kv, seq_ids, n_seqs, &need);
+  if (rc) return rc;
+  if (ws_bytes < need) {
+    set_error("oscar_decode_step: workspace %zu < %zu bytes", ws_bytes, need);
+    return OSCAR_E_WORKSPACE;
+  }
+  // ---- commit
+  std::vector<std::pair<int32_t, int32_t>> upd;
+  std::vector<StepSeq> plan = commit_step_write(kv, seq_ids, n_seqs, upd);
+  if (kv->plan_only) return OSCAR_OK;
+  hipStream_t st = as_stream(stream);
+  rc = push_table(kv, upd, st);
+  if (rc) return rc;
+  if (kv->decode_kernel == 1) {
+    // the reference kernel has no query preparation to share a launch with
+    for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+      const StepArgs a = step_args(kv, k, v, plan, c0, std::min(CHUNK, n_seqs - c0));
+      hipError_t e = launch_step_write(a, st);
+      if (e != hipSuccess) return hip_fail(e, "oscar_decode_step: launch");
+    }
+    return launch_decode(kv, seq_ids, n_seqs, nullptr, q, sm_scale, out, ws, st, "oscar_decode_step");
+  }
+  return launch_decode(kv, seq_ids, n_seqs, &plan, q, sm_scale, out, ws, st, "oscar_decode_step", k, v);
 }
 
 int oscar_kv_seq_info(const oscar_kv* kv, int32_t seq, int64_t* len, int64_t* n_int2) {

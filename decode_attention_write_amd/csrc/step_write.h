@@ -1,0 +1,106 @@
+// Device routines of the decode step's write, shared by the write kernels and the fused
+// decode-step kernel (write + query preparation in one launch).
+//
+// Method: axbrief, "Together AI's OSCAR breaks the 2-bit KV cache accuracy barrier", section
+// "어텐션 통계 기반 회전과 Triton 커널의 결합" (every new key rotated by R_K, clipped and
+// quantized to INT2); recent tokens stay BF16 and the oldest window token moves to INT2
+// (techllm, "KV cache compression", section "OSCAR").
+#pragma once
+
+#include "common.h"
+
+namespace oscar {
+
+// ------------------------------------------------------------------ eviction
+// One token of one (sequence, KV head) moves from the window to INT2: INT2 index i takes ring
+// slot 64 + i % 256 (the oldest window token).  256 threads; uses LDS scratch codes/meta.
+__device__ inline void evict_one(uint8_t* pool, const uint16_t* ring, const int32_t* page_table, int hkv,
+                                 int max_pages, int seq, int kvh, int i, uint8_t (*codes)[D], uint16_t* meta) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t ring_head = (static_cast<size_t>(seq) * hkv + kvh) * 2 * RING * D;
+  const int slot = i & (PAGE - 1);
+  const int page = page_table[static_cast<size_t>(seq) * max_pages + i / PAGE];
+  uint32_t* blk = reinterpret_cast<uint32_t*>(pool + (static_cast<size_t>(page) * hkv + kvh) * HEAD_BLOCK);
+  if (slot == 0) {
+    for (int w = tid; w < HEAD_BLOCK / 4; w += 256) blk[w] = 0;
+    __threadfence_block();
+  }
+  __syncthreads();
+  const int rs = SINK + (i % WIN);
+  // wave wv: task (isv = wv >> 1, group = wv & 1); lane holds one channel
+  const int isv = wv >> 1, g = wv & 1, c = 64 * g + lane;
+  const float xv = bf16_to_f32(ring[ring_head + (static_cast<size_t>(isv) * RING + rs) * D + c]);
+  float mn = xv, mx = xv;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  }
+  const QParams q = quant_params(mn, mx, isv ? C_V : C_K);
+  codes[isv][c] = (q.s16 != 0) ? static_cast<uint8_t>(quant_code(xv, q)) : 0;
+  if (lane == 0) {
+    meta[4 * isv + 2 * g] = q.s16;
+    meta[4 * isv + 2 * g + 1] = q.lo16;
+  }
+  __syncthreads();
+  if (tid < 8) {
+    // key words of this token: (g, kq) -> word kc_word(slot, 64 g + 16 kq)
+    const int gg = tid >> 2, kq = tid & 3;
+    uint32_t word = 0;
+    for (int u = 0; u < 16; ++u) {
+      const int cc = 64 * gg + 16 * kq + u;
+      word |= static_cast<uint32_t>(codes[0][cc]) << kc_bit(cc);
+    }
+    blk[(KC_OFF >> 2) + kc_word(slot, 64 * gg + 16 * kq)] = word;
+  } else if (tid < 8 + D) {
+    // value word of channel cc: read-modify-write of this token's 2 bits
+    const int cc = tid - 8;
+    uint32_t* wp = blk + (VC_OFF >> 2) + vc_word(slot, cc);
+    const int b = vc_bit(slot);
+    *wp = (*wp & ~(3u << b)) | (static_cast<uint32_t>(codes[1][cc]) << b);
+  } else if (tid < 8 + D + 4) {
+    const int m = tid - 8 - D;
+    blk[(META_OFF >> 2) + 4 * slot + m] = static_cast<uint32_t>(meta[2 * m]) | (static_cast<uint32_t>(meta[2 * m + 1]) << 16);
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ decode-step write
+// One (KV head, sequence of the chunk) per 256-thread work-group: the eviction of k_evict (when
+// the window is full) and the single-token append of k_append.  The new token's loads
+// (key, value, column c of R_K for thread c < 128) are issued first so that their latency
+// overlaps the eviction; the new token lands in the ring slot the eviction has just read
+// (window position 64 + n_int2 + 256 maps to slot 64 + n_int2 % 256), so it is written only
+// after the eviction's barrier.
+__device__ inline void step_write_block(const StepArgs& a, int kvh, int sl) {
+  const int tid = threadIdx.x;
+  const StepSeq sq = a.seqs[sl];
+  __shared__ uint8_t codes[2][D];
+  __shared__ uint16_t meta[8];
+  __shared__ float kin[D];
+  const size_t src = (static_cast<size_t>(sq.src) * a.hkv + kvh) * D;
+  float rc[D];
+  uint16_t vraw = 0;
+  if (tid < D) {
+    const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
+#pragma unroll
+    for (int i = 0; i < D; ++i) rc[i] = rot[i * D + tid];   // column tid of R
+    kin[tid] = bf16_to_f32(a.k[src + tid]);
+    vraw = a.v[src + tid];
+  }
+  if (sq.evict) evict_one(a.pool, a.ring, a.page_table, a.hkv, a.max_pages, sq.seq, kvh, sq.n_int2, codes, meta);
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
+    const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
+    const int p = sq.len0;
+    const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
+    a.ring[ring_head + static_cast<size_t>(slot) * D + tid] = f32_to_bf16(acc);
+    a.ring[ring_head + static_cast<size_t>(RING + slot) * D + tid] = vraw;
+  }
+}
+
+}  // namespace oscar

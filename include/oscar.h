@@ -271,6 +271,29 @@ int oscar_decode_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int
 int oscar_decode_attn(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *q,
                       float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Device workspace bytes oscar_decode_step needs for these sequences: the
+ * attention's workspace on the state after the step's write. */
+int oscar_decode_step_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs,
+                                      size_t *bytes);
+
+/*
+ * One whole decode step per listed (non-empty) sequence in one call: the
+ * decode-step write (as oscar_kv_decode_write: evict the oldest window token
+ * when the window holds 256, then append k, v) followed by decode attention
+ * over everything stored, the new token included (as oscar_decode_attn).  The
+ * stored state and the output equal those of the two calls ([A] rotation
+ * section: new tokens are rotated and quantized on write, and the read path is
+ * one fused pass; the write shares the launch of the query preparation).
+ * k, v      device bf16 [n_seqs][num_kv_heads][128], row i for seq_ids[i].
+ * q         device bf16 [n_seqs][num_q_heads][128] (unrotated queries).
+ * out       device fp32 [n_seqs][num_q_heads][128], in the R_V basis.
+ * ws        device workspace of at least oscar_decode_step_workspace_bytes bytes.
+ * Errors: OSCAR_E_ARG, OSCAR_E_STATE (an empty sequence, or no rotation),
+ * OSCAR_E_NOPAGE, OSCAR_E_WORKSPACE; nothing is changed on error.
+ */
+int oscar_decode_step(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *k, const void *v,
+                      const void *q, float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Length and INT2 token count of one sequence. */
 int oscar_kv_seq_info(const oscar_kv *kv, int32_t seq, int64_t *len, int64_t *n_int2);
 

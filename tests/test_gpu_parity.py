@@ -284,6 +284,62 @@ def test_fused_decode_write_matches_evict_then_write(gpu_lib):
 
 
 @pytest.mark.parametrize("kernel", [0, 1])
+def test_decode_step_one_call_matches_two_calls(gpu_lib, kernel):
+    """oscar_decode_step (the decode-step write sharing the query preparation's launch, then the
+    attention) leaves pool, ring and page table bit-identical to oscar_kv_decode_write followed by
+    oscar_decode_attn, and in the deterministic mode gives bit-identical outputs, over steps that
+    fill the window, evict across an INT2 page boundary and take new pages; the outputs match the
+    oracle on the GPU's exported state and end to end."""
+    hkv, hq = 2, 8
+    starts = {0: 10, 1: 300, 2: 400, 3: 320 + 127}
+    ids = [3, 1, 0, 2]
+    _case(f"one-call decode step vs decode-step write + attention, kernel {kernel}")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 5, hkv)
+    free = synth.page_permutation(synth.CFG_QWEN3_4B, 5, 16)
+    one = _store(gpu_lib, hq, hkv, 4, 8, 16, free, rot)
+    two = _store(gpu_lib, hq, hkv, 4, 8, 16, free, rot)
+    for st in (one, two):
+        st.set_decode_kernel(kernel)
+        st.set_decode_deterministic(True)
+    ora = ostore.OracleStore(hkv, 4, 8, 16, free, rot)
+    n_steps = 70
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, ids, hkv, max(starts.values()) + n_steps)
+    row = {s: b for b, s in enumerate(ids)}
+    for s, n in starts.items():
+        kb, vb = ks[row[s]:row[s] + 1, :n], vs[row[s]:row[s] + 1, :n]
+        for st in (one, two):
+            st.write([s], parity.to_dev_bf16(kb), parity.to_dev_bf16(vb))
+        ora.write([s], kb, vb)
+    pos = dict(starts)
+    for step in range(n_steps):
+        kt = np.stack([ks[row[s], pos[s]] for s in ids])       # [n_seqs, Hkv, 128]
+        vt = np.stack([vs[row[s], pos[s]] for s in ids])
+        q = synth.decode_queries(synth.CFG_QWEN3_4B, 5, 4, hq, hkv, step=step)
+        kd, vd, qd = parity.to_dev_bf16(kt), parity.to_dev_bf16(vt), parity.to_dev_bf16(q)
+        full = [s for s in ids if int(ora.length[s]) - 64 - int(ora.n_int2[s]) == 256]
+        if full:
+            ora.evict(full, 1)
+        ora.write(ids, kt[:, None], vt[:, None])
+        out1 = one.decode_step(ids, kd, vd, qd, SCALE).cpu().numpy()
+        two.decode_write(ids, kd, vd)
+        out2 = two.decode(ids, qd, SCALE).cpu().numpy()
+        for s in ids:
+            pos[s] += 1
+        assert np.array_equal(out1, out2), step
+        a, b = parity.export(one), parity.export(two)
+        for x, y, name in zip(a, b, ("pool", "ring", "table")):
+            assert np.array_equal(x, y), (step, name)
+        for s in ids:
+            assert one.seq_info(s) == (int(ora.length[s]), int(ora.n_int2[s]))
+        if step % 23 == 0 or step == n_steps - 1:
+            iso = attention.decode(a[0], a[1], a[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
+            assert parity.rel_l2(out1, iso) <= ISO_TOL, step
+            ref = attention.decode_store(ora, q, ids, SCALE, hq)
+            assert parity.rel_l2(out1, ref) <= E2E_TOL, step
+    assert np.array_equal(parity.export(one)[2], ora.page_table)
+
+
+@pytest.mark.parametrize("kernel", [0, 1])
 def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
     """Outputs do not depend on the split size (beyond rounding), repeat bitwise, and do not depend
     on where the pages sit in the pool.  The fp32 reference kernel (1) agrees across splits to 1e-6;

@@ -122,6 +122,35 @@ def test_errors_leave_state_unchanged():
     assert e.value.status == oscar.E_STATE
 
 
+def test_decode_step_plan_and_errors():
+    """The one-call decode step advances the host state exactly as the decode-step write, sizes its
+    workspace for the state after that write, and changes nothing when it fails."""
+    a, b = _plan_store(max_pages=8, num_pages=12), _plan_store(max_pages=8, num_pages=12)
+    for s in (a, b):
+        s.write([0], None, None, n_new=320 + 64 * 2)   # window full, INT2 index 128: next evict takes a page
+        s.write([1], None, None, n_new=100)
+    ids = [0, 1]
+    # the step's workspace is the attention's workspace after the write
+    need = a.step_workspace_bytes(ids)
+    b.decode_write(ids, None, None)
+    assert need == b.workspace_bytes(ids)
+    state = (a.seq_info(0), a.seq_info(1), a.page_table().copy(), a.free_pages().copy())
+    # plan-only stores pass no workspace: the size check fails first and nothing moves
+    with pytest.raises(oscar.OscarError) as e:
+        oscar.oscar_decode_step(a, ids, None, None, None, 0.1, None, None)
+    assert e.value.status == oscar.E_WORKSPACE
+    assert (a.seq_info(0), a.seq_info(1)) == state[:2]
+    assert np.array_equal(a.page_table(), state[2]) and np.array_equal(a.free_pages(), state[3])
+    # an empty sequence, a bad id and a non-finite scale are refused before anything changes
+    for bad_ids, scale, status in (([0, 2], 0.1, oscar.E_STATE), ([0, 9], 0.1, oscar.E_ARG),
+                                   (ids, float("nan"), oscar.E_ARG)):
+        with pytest.raises(oscar.OscarError) as e:
+            oscar.oscar_decode_step(a, bad_ids, None, None, None, scale, None, None)
+        assert e.value.status == status
+        assert (a.seq_info(0), a.seq_info(1)) == state[:2]
+        assert np.array_equal(a.free_pages(), state[3])
+
+
 def test_workspace_bytes_and_split_choice():
     s = _plan_store(max_pages=64, num_pages=64)
     s.write([0], None, None, n_new=320 + 64 * 20)
