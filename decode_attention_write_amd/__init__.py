@@ -42,7 +42,7 @@ EXPORTS = [
     "oscar_kv_set_decode_deterministic",
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
-    "oscar_decode_step_workspace_bytes", "oscar_decode_step",
+    "oscar_decode_step_workspace_bytes", "oscar_decode_step", "oscar_kv_set_write_evicts",
 ]
 
 
@@ -95,6 +95,7 @@ def load():
         "oscar_kv_read_timing": [P, I32, P, P, P],
         "oscar_decode_step_workspace_bytes": [P, P, I32, P],
         "oscar_decode_step": [P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P],
+        "oscar_kv_set_write_evicts": [P, I32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -277,6 +278,10 @@ class KVStore:
             _check(load().oscar_kv_write(self.handle, p, len(ids), int(n_new), None, None, None))
             return
         oscar_kv_write(self, seq_ids, k, v, stream)
+
+    def set_write_evicts(self, on):
+        """Let writes overflow a non-empty window, evicting as they go (chunked prefill)."""
+        _check(load().oscar_kv_set_write_evicts(self.handle, 1 if on else 0))
 
     def evict(self, seq_ids, n_evict=1, stream=None):
         oscar_kv_evict_window(self, seq_ids, n_evict, stream)

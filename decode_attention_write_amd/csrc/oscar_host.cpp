@@ -46,6 +46,7 @@ struct oscar_kv {
   int32_t pages_per_split = 0;
   int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
   int32_t deterministic = 0;   // 1: fixed page range per split (no sharing between splits)
+  int32_t write_evicts = 0;    // 1: a write that overflows a non-empty window evicts as it goes
   bool has_rotation = false;
   // timing events per timed kernel: 2 * OSCAR_TIMING_PAIRS each when timing is on
   std::vector<hipEvent_t> timing_ev[2];
@@ -181,6 +182,13 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
     best = std::max(best, pps);
   }
   return best;
+}
+
+// Evictions a write of n_new tokens into the non-empty sequence s needs: the sink and window
+// hold 320 - (len - n_int2) more tokens; every token beyond that first moves the oldest window
+// token into INT2.
+int64_t overflow_evictions(const oscar_kv* kv, int s, int64_t n_new) {
+  return std::max<int64_t>(0, n_new - (kRing - (kv->len[s] - kv->n_int2[s])));
 }
 
 // ---- decode-step write and decode attention, shared by the one-call and two-call forms
@@ -443,12 +451,19 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
       }
       need += pages;
     } else {
-      const int64_t new_len = kv->len[s] + n_new;
-      const int64_t win = std::max<int64_t>(0, new_len - kSink - kv->n_int2[s]);
-      if (win > kWin) {
-        set_error("oscar_kv_write: window of sequence %d would hold %lld > 256 tokens", s, static_cast<long long>(win));
+      const int64_t e = overflow_evictions(kv, s, n_new);
+      if (e > 0 && !kv->write_evicts) {
+        set_error("oscar_kv_write: window of sequence %d would hold %lld > 256 tokens", s,
+                  static_cast<long long>(kWin + e));
         return OSCAR_E_WINDOW_FULL;
       }
+      const int64_t n2 = kv->n_int2[s];
+      if (ceil_div(n2 + e, kPage) > maxp) {
+        set_error("oscar_kv_write: sequence %d would need %lld pages > max_pages_per_seq", s,
+                  static_cast<long long>(ceil_div(n2 + e, kPage)));
+        return OSCAR_E_NOPAGE;
+      }
+      need += ceil_div(n2 + e, kPage) - ceil_div(n2, kPage);
     }
   }
   if (need > static_cast<int64_t>(kv->fifo.size())) {
@@ -457,10 +472,26 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
   }
   // ---- commit: allocate pages, update mirrors
   std::vector<std::pair<int32_t, int32_t>> upd;
-  std::vector<WriteSeq> plan(n_seqs);
+  std::vector<WriteSeq> plan, over;   // plain writes; writes that evict as they go
+  std::vector<int64_t> over_n2;       // INT2 count before the call, per evicting write
   for (int i = 0; i < n_seqs; ++i) {
     const int s = seq_ids[i];
-    plan[i] = WriteSeq{s, static_cast<int32_t>(kv->len[s]), i, 0};
+    const int64_t e = (kv->len[s] == 0) ? 0 : overflow_evictions(kv, s, n_new);
+    if (e > 0) {
+      over.push_back(WriteSeq{s, static_cast<int32_t>(kv->len[s]), i, 0});
+      over_n2.push_back(kv->n_int2[s]);
+      for (int64_t p = ceil_div(kv->n_int2[s], kPage); p < ceil_div(kv->n_int2[s] + e, kPage); ++p) {
+        const int32_t page = kv->fifo.front();
+        kv->fifo.pop_front();
+        const int32_t idx = static_cast<int32_t>(s * maxp + p);
+        kv->table[idx] = page;
+        upd.emplace_back(idx, page);
+      }
+      kv->n_int2[s] += e;
+      kv->len[s] += n_new;
+      continue;
+    }
+    plan.push_back(WriteSeq{s, static_cast<int32_t>(kv->len[s]), i, 0});
     if (kv->len[s] == 0) {
       const int64_t n2 = std::max<int64_t>(0, n_new - kRing);
       for (int64_t p = 0; p < ceil_div(n2, kPage); ++p) {
@@ -481,8 +512,9 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
   const int n_tiles = static_cast<int>(ceil_div(n_new, kPage));
   // a call that produces no INT2 token (appends, short first writes) takes the per-token kernel
   bool any_int2 = false;
-  for (int i = 0; i < n_seqs; ++i) any_int2 |= (plan[i].len0 == 0 && n_new > kRing);
-  for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
+  for (const WriteSeq& w : plan) any_int2 |= (w.len0 == 0 && n_new > kRing);
+  const int n_plain = static_cast<int>(plan.size());
+  for (int c0 = 0; c0 < n_plain; c0 += CHUNK) {
     WriteArgs a{};
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -493,7 +525,7 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
     a.hkv = kv->desc.num_kv_heads;
     a.max_pages = kv->desc.max_pages_per_seq;
     a.n_new = n_new;
-    a.n_seqs = std::min(CHUNK, n_seqs - c0);
+    a.n_seqs = std::min(CHUNK, n_plain - c0);
     for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
     const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_WRITE);
     hipError_t e = t0 ? hipEventRecord(t0, st) : hipSuccess;
@@ -501,6 +533,58 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
     if (e == hipSuccess && t1) e = hipEventRecord(t1, st);
     if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
   }
+  // Writes that overflow a non-empty window, one sequence at a time: the tokens that fit, then
+  // rounds of (evict the c oldest window tokens, append the next c tokens), c <= 256.  The c
+  // tokens of a round land in the ring slots its eviction has just read, so each round equals c
+  // alternations of single-token eviction and append.
+  const size_t row = static_cast<size_t>(kv->desc.num_kv_heads) * OSCAR_HEAD_DIM;
+  for (size_t j = 0; j < over.size(); ++j) {
+    const WriteSeq& w = over[j];
+    int64_t len = w.len0, n2 = over_n2[j], t0 = 0;
+    while (t0 < n_new) {
+      const int64_t room = kRing - (len - n2);   // free sink + window slots
+      const int64_t c = (room > 0) ? std::min<int64_t>(room, n_new - t0) : std::min<int64_t>(kWin, n_new - t0);
+      hipError_t e = hipSuccess;
+      if (room <= 0) {
+        EvictArgs ea{};
+        ea.pool = static_cast<uint8_t*>(kv->desc.pool);
+        ea.ring = static_cast<uint16_t*>(kv->desc.ring);
+        ea.page_table = kv->desc.page_table;
+        ea.hkv = kv->desc.num_kv_heads;
+        ea.max_pages = kv->desc.max_pages_per_seq;
+        ea.n_evict = static_cast<int32_t>(c);
+        ea.n_seqs = 1;
+        ea.seqs[0] = EvictSeq{w.seq, static_cast<int32_t>(n2)};
+        e = launch_evict(ea, st);
+        n2 += c;
+      }
+      if (e == hipSuccess) {
+        WriteArgs a{};
+        const size_t off = (static_cast<size_t>(w.src) * n_new + t0) * row;
+        a.k = static_cast<const uint16_t*>(k) + off;
+        a.v = static_cast<const uint16_t*>(v) + off;
+        a.pool = static_cast<uint8_t*>(kv->desc.pool);
+        a.ring = static_cast<uint16_t*>(kv->desc.ring);
+        a.page_table = kv->desc.page_table;
+        a.rot = static_cast<const uint8_t*>(kv->desc.rot);
+        a.hkv = kv->desc.num_kv_heads;
+        a.max_pages = kv->desc.max_pages_per_seq;
+        a.n_new = static_cast<int32_t>(c);
+        a.n_seqs = 1;
+        a.seqs[0] = WriteSeq{w.seq, static_cast<int32_t>(len), 0, 0};
+        e = launch_append(a, st);
+      }
+      if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
+      len += c;
+      t0 += c;
+    }
+  }
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_write_evicts(oscar_kv* kv, int32_t on) {
+  if (!kv || (on != 0 && on != 1)) { set_error("oscar_kv_set_write_evicts: bad handle or value"); return OSCAR_E_ARG; }
+  kv->write_evicts = on;
   return OSCAR_OK;
 }
 

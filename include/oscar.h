@@ -218,14 +218,26 @@ int oscar_kv_set_rotation(oscar_kv *kv, const float *rot_host, void *stream);
  * BF16 sink, positions 64 .. L-257 are quantized straight to INT2 (from the
  * fp32 rotated key) and the last min(L-64, 256) positions go to the BF16
  * window.  Into a non-empty sequence, positions < 64 go to the sink and the
- * rest to the window.  Pages are taken from the FIFO in seq_ids order,
- * ascending within a sequence.
+ * rest to the window; when they do not fit (the sink and window hold 320
+ * tokens) and oscar_kv_set_write_evicts is on, each token that does not fit
+ * first moves the oldest window token into INT2, as oscar_kv_evict_window
+ * would (from its stored bf16 copy): the stored state equals that of writing
+ * the tokens one at a time with an eviction whenever the window is full
+ * (techllm "KV cache compression", OSCAR section: recent tokens BF16, older
+ * history INT2).  Pages are taken from the FIFO in seq_ids order, ascending
+ * within a sequence.
  * Errors: OSCAR_E_ARG, OSCAR_E_WINDOW_FULL (a non-empty sequence's window
- * would exceed 256 tokens: evict first), OSCAR_E_NOPAGE (FIFO too short or a
- * sequence would exceed max_pages_per_seq).
+ * would exceed 256 tokens and evicting writes are off: evict first),
+ * OSCAR_E_NOPAGE (FIFO too short or a sequence would exceed
+ * max_pages_per_seq); nothing is changed on error.
  */
 int oscar_kv_write(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t n_new,
                    const void *k, const void *v, void *stream);
+
+/* Evicting writes (chunked prefill): on = 1 lets oscar_kv_write overflow a
+ * non-empty sequence's window, evicting as it goes (see above); on = 0
+ * (default) returns OSCAR_E_WINDOW_FULL instead.  Errors: OSCAR_E_ARG. */
+int oscar_kv_set_write_evicts(oscar_kv *kv, int32_t on);
 
 /*
  * Move the n_evict oldest window tokens of each listed sequence into INT2

@@ -85,6 +85,8 @@ class OracleStore:
         self.page_table = np.full((max_seqs, max_pages_per_seq), -1, dtype=np.int32)
         self.length = np.zeros(max_seqs, dtype=np.int64)
         self.n_int2 = np.zeros(max_seqs, dtype=np.int64)
+        # a write that overflows a non-empty window evicts token by token (else "window full")
+        self.write_evicts = False
 
     # ------------------------------------------------------------------ helpers
     def window_count(self, seq):
@@ -134,9 +136,14 @@ class OracleStore:
                 if -(-n_int2 // PAGE) > self.max_pages:
                     raise StoreError("too many pages for one sequence")
             else:
-                new_len = L0 + n_new
-                if max(0, new_len - SINK - int(self.n_int2[s])) > WINDOW:
+                # tokens beyond the free sink + window slots each evict the oldest window token
+                evictions = max(0, n_new - (RING_SLOTS - (L0 - int(self.n_int2[s]))))
+                if evictions and not self.write_evicts:
                     raise StoreError("window full")
+                n2 = int(self.n_int2[s])
+                if -(-(n2 + evictions) // PAGE) > self.max_pages:
+                    raise StoreError("too many pages for one sequence")
+                need += -(-(n2 + evictions) // PAGE) - -(-n2 // PAGE)
         if need > len(self.free):
             raise StoreError("out of pages")
         for b, s in enumerate(seq_ids):
@@ -161,10 +168,12 @@ class OracleStore:
             else:
                 for t in range(n_new):
                     p = L0 + t
+                    if p >= SINK and self.window_count(s) == WINDOW:
+                        self.evict([s], 1)                    # the oldest window token moves to INT2
                     slot = self.ring_slot(p)
                     self.ring[s, :, 0, slot] = kx_bf[t]
                     self.ring[s, :, 1, slot] = v_bits[b, t]
-                self.length[s] = L0 + n_new
+                    self.length[s] = p + 1
 
     def evict(self, seq_ids, n_evict):
         need = 0

@@ -283,6 +283,59 @@ def test_fused_decode_write_matches_evict_then_write(gpu_lib):
     assert parity.rel_l2(out, ref) <= E2E_TOL
 
 
+def test_evicting_write_matches_token_by_token(gpu_lib):
+    """Chunked prefill: a write that overflows a non-empty window, with evicting writes on, leaves
+    pool, ring and page table bit-identical to writing the same tokens one at a time through the
+    decode-step write (evict when the window is full, append); page tables equal the oracle's and
+    decode over the result matches the oracle (same chunked writes) end to end."""
+    hkv, hq = 2, 8
+    _case("evicting (chunked) write vs token-by-token decode-step writes")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 6, hkv)
+    free = synth.page_permutation(synth.CFG_QWEN3_4B, 6, 48)
+    chunked = _store(gpu_lib, hq, hkv, 3, 16, 48, free, rot)
+    chunked.set_write_evicts(True)
+    single = _store(gpu_lib, hq, hkv, 3, 16, 48, free, rot)
+    ora = ostore.OracleStore(hkv, 3, 16, 48, free, rot)
+    ora.write_evicts = True
+    # (sequences, tokens) per call: first writes, then overflows from a partly filled sink, a partly
+    # filled window, a full window (several 256-token rounds), and a two-sequence call
+    calls = [([0], 100), ([1], 10), ([0], 150), ([1], 700), ([0], 37), ([2], 400), ([0], 300),
+             ([1, 2], 333)]
+    total = {0: 0, 1: 0, 2: 0}
+    for ids, n in calls:
+        for s_ in ids:
+            total[s_] += n
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, [0, 1, 2], hkv, max(total.values()))
+    pos = {0: 0, 1: 0, 2: 0}
+    for ids, n in calls:
+        kb = np.stack([ks[s_, pos[s_]:pos[s_] + n] for s_ in ids])
+        vb = np.stack([vs[s_, pos[s_]:pos[s_] + n] for s_ in ids])
+        chunked.write(ids, parity.to_dev_bf16(kb), parity.to_dev_bf16(vb))
+        ora.write(ids, kb, vb)
+        for b, s_ in enumerate(ids):
+            if pos[s_] == 0:
+                single.write([s_], parity.to_dev_bf16(kb[b:b + 1]), parity.to_dev_bf16(vb[b:b + 1]))
+            else:
+                for t in range(n):
+                    single.decode_write([s_], parity.to_dev_bf16(kb[b:b + 1, t]), parity.to_dev_bf16(vb[b:b + 1, t]))
+            pos[s_] += n
+        a, b_ = parity.export(chunked), parity.export(single)
+        for x, y, name in zip(a, b_, ("pool", "ring", "table")):
+            assert np.array_equal(x, y), (ids, n, name)
+        for s_ in (0, 1, 2):
+            assert chunked.seq_info(s_) == single.seq_info(s_) == (int(ora.length[s_]), int(ora.n_int2[s_]))
+        assert np.array_equal(a[2], ora.page_table)
+        assert np.array_equal(chunked.free_pages(), np.array(list(ora.free), dtype=np.int32))
+    seqs = [0, 1, 2]
+    q = synth.decode_queries(synth.CFG_QWEN3_4B, 6, 3, hq, hkv)
+    out = chunked.decode(seqs, parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    gpu = parity.export(chunked)
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
+    assert parity.rel_l2(out, iso) <= ISO_TOL
+    ref = attention.decode_store(ora, q, seqs, SCALE, hq)
+    assert parity.rel_l2(out, ref) <= E2E_TOL
+
+
 @pytest.mark.parametrize("kernel", [0, 1])
 def test_decode_step_one_call_matches_two_calls(gpu_lib, kernel):
     """oscar_decode_step (the decode-step write sharing the query preparation's launch, then the

@@ -122,6 +122,41 @@ def test_errors_leave_state_unchanged():
     assert e.value.status == oscar.E_STATE
 
 
+def test_evicting_write_plan_matches_oracle():
+    """With evicting writes on, overflowing writes into non-empty sequences take pages exactly as the
+    oracle's token-by-token eviction does (FIFO order across the call's sequences, ascending within
+    a sequence); with them off the same call is refused; a short FIFO refuses it unchanged."""
+    free = list(np.random.default_rng(7).permutation(48))
+    s = _plan_store(max_seqs=3, max_pages=32, num_pages=48, free=free)
+    o = _oracle_store(max_seqs=3, max_pages=32, num_pages=48, free=free)
+    zeros = lambda n, k=1: np.zeros((k, n, 2, 128), dtype=np.uint16)  # noqa: E731
+    for ids, n in (([0], 100), ([1], 400), ([0], 200)):
+        s.write(ids, None, None, n_new=n)
+        o.write(ids, zeros(n, len(ids)), zeros(n, len(ids)))
+    with pytest.raises(oscar.OscarError) as e:
+        s.write([0, 1], None, None, n_new=300)
+    assert e.value.status == oscar.E_WINDOW_FULL
+    s.set_write_evicts(True)
+    o.write_evicts = True
+    for ids, n in (([0, 1], 300), ([1], 1000), ([0], 1), ([2], 5), ([2, 0], 640)):
+        s.write(ids, None, None, n_new=n)
+        o.write(ids, zeros(n, len(ids)), zeros(n, len(ids)))
+        assert np.array_equal(s.page_table(), o.page_table), (ids, n)
+        assert list(s.free_pages()) == list(o.free)
+        for q in range(3):
+            assert s.seq_info(q) == (int(o.length[q]), int(o.n_int2[q]))
+            L, n2 = s.seq_info(q)
+            # store invariants: the window never holds more than 256 tokens; one page per 64 INT2
+            assert 0 <= L - min(L, 64) - n2 <= 256
+            assert (s.page_table()[q] >= 0).sum() == -(-n2 // 64)
+    snap = (s.page_table().copy(), list(s.free_pages()), [s.seq_info(q) for q in range(3)])
+    with pytest.raises(oscar.OscarError) as e:
+        s.write([1], None, None, n_new=64 * 30)      # more pages than the FIFO holds
+    assert e.value.status in (oscar.E_NOPAGE,)
+    assert np.array_equal(s.page_table(), snap[0]) and list(s.free_pages()) == snap[1]
+    assert [s.seq_info(q) for q in range(3)] == snap[2]
+
+
 def test_decode_step_plan_and_errors():
     """The one-call decode step advances the host state exactly as the decode-step write, sizes its
     workspace for the state after that write, and changes nothing when it fails."""

@@ -306,6 +306,35 @@ def test_store_allocator_fifo_order_and_errors():
     assert L[0] == 64 + n2[0] + st.window_count(0)
 
 
+def test_evicting_write_is_token_by_token_evict_and_append():
+    """An overflowing write with evicting writes on reaches the state of appending its tokens one at
+    a time with an explicit one-token eviction whenever the window holds 256 (the decode step's
+    order), with 320 tokens left BF16; a token that fits never evicts."""
+    rot = _rot()
+    kb, vb = synth.unit_kv(synth.CFG_TINY, 0, 0, 0, 1500)
+    K, V = kb[None, :, None, :], vb[None, :, None, :]
+    a = store.OracleStore(1, 1, 32, 32, range(32), rot)
+    b = store.OracleStore(1, 1, 32, 32, range(32), rot)
+    a.write_evicts = True
+    for st in (a, b):
+        st.write([0], K[:, :40], V[:, :40])
+    a.write([0], K[:, 40:900], V[:, 40:900])           # sink fill, window fill, 540 evictions
+    a.write([0], K[:, 900:1500], V[:, 900:1500])
+    for t in range(40, 1500):
+        if b.window_count(0) == 256:
+            b.evict([0], 1)
+        b.write([0], K[:, t:t + 1], V[:, t:t + 1])
+    assert np.array_equal(a.pool, b.pool) and np.array_equal(a.ring, b.ring)
+    assert np.array_equal(a.page_table, b.page_table) and list(a.free) == list(b.free)
+    assert (a.length[0], a.n_int2[0], a.window_count(0)) == (1500, 1500 - 320, 256)
+    # a write that fits the free slots evicts nothing
+    c = store.OracleStore(1, 1, 32, 32, range(32), rot)
+    c.write_evicts = True
+    c.write([0], K[:, :10], V[:, :10])
+    c.write([0], K[:, 10:320], V[:, 10:320])
+    assert c.n_int2[0] == 0 and c.window_count(0) == 256
+
+
 def test_evict_quantizes_ring_value():
     rot = _rot()
     kb, vb = synth.unit_kv(synth.CFG_TINY, 0, 0, 0, 320)
