@@ -230,7 +230,7 @@ def prefill_leg(reps=5):
     return res
 
 
-def layer_leg(cfg, hq, hkv, lengths, reps, label):
+def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0):
     """One attention layer over sequences of the given lengths (one R_K per KV head, pages in a
     seeded shuffled order): prefill writes, then `reps` decode steps (the decode-step write of
     one token per sequence, then decode attention), each after one untimed step.  Returns the
@@ -249,6 +249,7 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label):
     num_pages = sum(-(-(L + reps + 2) // 64) for L in lengths) + B
     st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, 0, num_pages))
     st.set_rotation(rots)
+    st.set_decode_split(pps)
     prm = sgpu.HeadParams(cfg, 0, hkv)
     n_new = reps + 1
     kbuf = torch.empty((1, max(lengths) + n_new, hkv, 128), dtype=torch.int16, device="cuda")
@@ -329,6 +330,8 @@ def main():
     ap.add_argument("--deterministic", action="store_true",
                     help="fixed page range per split (no page sharing between the splits of a unit)")
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
+    ap.add_argument("--layer-pps", type=int, default=0,
+                    help="development: pages per decode split in the single-layer legs (0 = library choice)")
     ap.add_argument("--two-call", action="store_true",
                     help="development: the decode-step write and the attention as two calls")
     ap.add_argument("--separate-write", action="store_true",
@@ -597,10 +600,11 @@ def main():
     if not args.no_layers:
         result["layer_qwen3_4b_32k_b8"] = layer_leg(
             synth.CFG_QWEN3_4B, 32, 8, [32768] * 8, 20,
-            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context")
+            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context", pps=args.layer_pps)
         result["layer_qwen3_32b_ragged_b16"] = layer_leg(
             synth.CFG_QWEN3_32B, 64, 8, [int(x) for x in synth.ragged_lengths(synth.CFG_QWEN3_32B, 16, 8192, 131072)],
-            20, "qwen3-32b-shaped layer: 64 q / 8 kv heads (GQA 8), batch 16, lengths U[8192, 131072]")
+            20, "qwen3-32b-shaped layer: 64 q / 8 kv heads (GQA 8), batch 16, lengths U[8192, 131072]",
+            pps=args.layer_pps)
     if args.copy_calib_mib:
         # a plain copy of known size, for scaling the memory counters of a profiled run
         n = args.copy_calib_mib * (1 << 20) // 4

@@ -283,6 +283,62 @@ def test_fused_decode_write_matches_evict_then_write(gpu_lib):
     assert parity.rel_l2(out, ref) <= E2E_TOL
 
 
+def _extreme_tokens(rng, n):
+    """fp32 [n, 128] rows whose 64-channel groups cycle through the quantizer's edge cases."""
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    for t in range(n):
+        for g in range(2):
+            sl = slice(64 * g, 64 * g + 64)
+            kind = (2 * t + g) % 7
+            if kind == 0:
+                x[t, sl] = 1.5                                          # constant: s16 = 0
+            elif kind == 1:
+                x[t, sl] = 0.0                                          # all zero
+            elif kind == 2:
+                x[t, sl] = 1e-8 * (1 + rng.random(64))                  # scale underflows fp16: s16 = 0
+            elif kind == 3:
+                x[t, sl] = 1e-5 * rng.standard_normal(64)               # fp16-denormal scale
+            elif kind == 4:
+                x[t, sl] = 100.0 + 0.5 * rng.random(64)                 # one-signed, far from zero
+            elif kind == 5:
+                x[t, sl] = 3e4 * np.tanh(rng.standard_normal(64))       # near the fp16 range limit
+            # kind 6: the Gaussian row as drawn
+    return x
+
+
+def test_degenerate_and_extreme_groups(gpu_lib):
+    """Quantizer edge cases through the whole path with an identity rotation (both sides quantize
+    identical fp32 inputs): constant and all-zero groups, scales that underflow fp16 (every code 0),
+    fp16-denormal scales, one-signed groups far from zero and groups near the fp16 limit; stored
+    state under the judge rules with no metadata flip, then evictions of such tokens and decode
+    parity on identical state, with finite outputs."""
+    hkv, hq, L = 1, 2, 320 + 64 * 3 + 17
+    _case("degenerate / extreme quantizer groups, identity rotation")
+    rot = np.eye(D, dtype=np.float32)[None]
+    rng = np.random.default_rng(11)
+    kb = synth.f32_to_bf16_bits(_extreme_tokens(rng, L + 40))[:, None, :]
+    vb = synth.f32_to_bf16_bits(_extreme_tokens(rng, L + 40))[:, None, :]
+    free = list(range(8))
+    gpu = _store(gpu_lib, hq, hkv, 1, 8, 8, free, rot)
+    ora = ostore.OracleStore(hkv, 1, 8, 8, free, rot)
+    gpu.write([0], parity.to_dev_bf16(kb[None, :L]), parity.to_dev_bf16(vb[None, :L]))
+    ora.write([0], kb[None, :L], vb[None, :L])
+    totals, _ = _check_state(parity.export(gpu), ora, [0], rot, {0: (kb[:L], vb[:L], L)})
+    assert totals["k_meta_flips"] == 0, totals
+    # evict 40 of these tokens from the GPU's ring: bit-exact against the oracle on that ring
+    ring_before = parity.export(gpu)[1]
+    gpu.evict([0], 40)
+    after = parity.export(gpu)
+    for i in range(40):
+        _check_evicted(after, ring_before, [0], hkv, L - 320 + i)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((1, hq, D)).astype(np.float32))
+    out = gpu.decode([0], parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    iso = attention.decode(after[0], after[1], after[2], np.array([L]), np.array([L - 320 + 40]), rot, q, [0],
+                           SCALE, hq)
+    assert parity.rel_l2(out, iso) <= ISO_TOL
+
+
 def test_evicting_write_matches_token_by_token(gpu_lib):
     """Chunked prefill: a write that overflows a non-empty window, with evicting writes on, leaves
     pool, ring and page table bit-identical to writing the same tokens one at a time through the
