@@ -339,6 +339,43 @@ def test_degenerate_and_extreme_groups(gpu_lib):
     assert parity.rel_l2(out, iso) <= ISO_TOL
 
 
+def test_more_sequences_than_one_launch(gpu_lib):
+    """70 sequences (a launch takes at most 64): one batched first write, then three one-call decode
+    steps (each evicting, pages crossing at INT2 index 128) and an attention call, all with the
+    sequences listed in a shuffled order; page tables and FIFO equal the oracle's and every
+    sequence's output row matches the oracle on the GPU's state."""
+    hkv, hq, n, L = 2, 8, 70, 320 + 125
+    _case(f"{n} sequences in one call (two launch chunks)")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 7, hkv)
+    n_pages = n * 3 + 4
+    free = synth.page_permutation(synth.CFG_QWEN3_4B, 7, n_pages)
+    st = _store(gpu_lib, hq, hkv, n, 4, n_pages, free, rot)
+    ora = ostore.OracleStore(hkv, n, 4, n_pages, free, rot)
+    ids = [int(x) for x in np.random.default_rng(3).permutation(n)]
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, ids, hkv, L + 3)
+    st.write(ids, parity.to_dev_bf16(ks[:, :L]), parity.to_dev_bf16(vs[:, :L]))
+    ora.write(ids, ks[:, :L], vs[:, :L])
+    for step in range(3):
+        q = synth.decode_queries(synth.CFG_QWEN3_4B, 7, n, hq, hkv, step=step)
+        out = st.decode_step(ids, parity.to_dev_bf16(ks[:, L + step]), parity.to_dev_bf16(vs[:, L + step]),
+                             parity.to_dev_bf16(q), SCALE).cpu().numpy()
+        ora.evict(ids, 1)
+        ora.write(ids, ks[:, L + step:L + step + 1], vs[:, L + step:L + step + 1])
+        gpu = parity.export(st)
+        assert np.array_equal(gpu[2], ora.page_table), step
+        assert np.array_equal(st.free_pages(), np.array(list(ora.free), dtype=np.int32)), step
+        iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
+        for b in range(n):
+            assert parity.rel_l2(out[b], iso[b]) <= ISO_TOL, (step, b, ids[b])
+    q = synth.decode_queries(synth.CFG_QWEN3_4B, 7, n, hq, hkv, step=9)
+    out = st.decode(ids[::-1], parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, ids[::-1], SCALE, hq)
+    for b in range(n):
+        assert parity.rel_l2(out[b], iso[b]) <= ISO_TOL, b
+    ref = attention.decode_store(ora, q, ids[::-1], SCALE, hq)
+    assert parity.rel_l2(out, ref) <= E2E_TOL
+
+
 def test_evicting_write_matches_token_by_token(gpu_lib):
     """Chunked prefill: a write that overflows a non-empty window, with evicting writes on, leaves
     pool, ring and page table bit-identical to writing the same tokens one at a time through the
