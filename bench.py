@@ -134,6 +134,9 @@ def cpu_baseline(units, rots, q_layer0, out_layer0, hq, hkv, total_units, step_b
     """
     import multiprocessing as mp
     import numpy as np
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        raise RuntimeError("the CPU-oracle leg spawns worker processes: run it outside the profiler "
+                           "(profiled runs take --no-cpu-baseline)")
     g = hq // hkv
     P = max(1, min(16, len(os.sched_getaffinity(0)), len(units)))
     jobs = [(L, n2, pool_u, ring_u, rots[0][kv:kv + 1], q_layer0[s:s + 1, kv * g:(kv + 1) * g], g)

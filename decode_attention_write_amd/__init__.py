@@ -43,6 +43,7 @@ EXPORTS = [
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
     "oscar_decode_step_workspace_bytes", "oscar_decode_step", "oscar_kv_set_write_evicts",
+    "oscar_kv_set_output_bf16",
 ]
 
 
@@ -96,6 +97,7 @@ def load():
         "oscar_decode_step_workspace_bytes": [P, P, I32, P],
         "oscar_decode_step": [P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P],
         "oscar_kv_set_write_evicts": [P, I32],
+        "oscar_kv_set_output_bf16": [P, I32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -234,6 +236,7 @@ class KVStore:
         self.hq, self.hkv = num_q_heads, num_kv_heads
         self.max_seqs, self.max_pages, self.num_pages = max_seqs, max_pages_per_seq, num_pages
         self.plan_only = plan_only
+        self.out_bf16 = False
         d = _Desc(num_q_heads, num_kv_heads, max_seqs, max_pages_per_seq, num_pages,
                   FLAG_PLAN_ONLY if plan_only else 0, None, None, None, None)
         sizes = [ctypes.c_size_t(0) for _ in range(4)]
@@ -279,6 +282,16 @@ class KVStore:
             return
         oscar_kv_write(self, seq_ids, k, v, stream)
 
+    def set_output_bf16(self, on):
+        """Decode outputs as bf16 (torch.bfloat16 tensors from decode / decode_step) instead of fp32."""
+        _check(load().oscar_kv_set_output_bf16(self.handle, 1 if on else 0))
+        self.out_bf16 = bool(on)
+
+    def _out(self, n, device):
+        import torch
+        return torch.empty((n, self.hq, HEAD_DIM), dtype=torch.bfloat16 if self.out_bf16 else torch.float32,
+                           device=device)
+
     def set_write_evicts(self, on):
         """Let writes overflow a non-empty window, evicting as they go (chunked prefill)."""
         _check(load().oscar_kv_set_write_evicts(self.handle, 1 if on else 0))
@@ -296,7 +309,7 @@ class KVStore:
         import torch
         n = len(seq_ids)
         if out is None:
-            out = torch.empty((n, self.hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+            out = self._out(n, q.device)
         if ws is None:
             ws = torch.empty(max(4, self.workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)
         oscar_decode_attn(self, seq_ids, q, sm_scale, out, ws, stream)
@@ -308,8 +321,7 @@ class KVStore:
     def decode_step(self, seq_ids, k, v, q, sm_scale, out=None, ws=None, stream=None):
         """The decode-step write and the decode attention in one call; returns out."""
         if out is None and not self.plan_only:
-            import torch
-            out = torch.empty((len(seq_ids), self.hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+            out = self._out(len(seq_ids), q.device)
         if ws is None and not self.plan_only:
             import torch
             ws = torch.empty(max(4, self.step_workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)

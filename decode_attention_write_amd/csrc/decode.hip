@@ -218,7 +218,9 @@ __global__ __launch_bounds__(128) void k_combine(DecodeArgs a) {
       O = fmaf(wsh[i], rec[2 + c], O);
     }
   }
-  a.out[(static_cast<size_t>(sq.src) * a.hq + h) * D + c] = O / L;
+  const size_t o = (static_cast<size_t>(sq.src) * a.hq + h) * D + c;
+  if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(O / L);
+  else a.out[o] = O / L;
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {

@@ -99,6 +99,7 @@ struct DecodeArgs {
   float scale_log2;       // sm_scale * log2(e)
   int32_t kernel;         // 0 matrix-core split kernel, 1 reference kernel (record layout)
   int32_t share;          // matrix-core kernel: 1 = splits of a unit share their pages, 0 = fixed ranges
+  int32_t out_bf16;       // 1: out holds bf16 (round to nearest even) instead of fp32
   DecodeSeq seqs[CHUNK];
 };
 

@@ -47,6 +47,7 @@ struct oscar_kv {
   int32_t decode_kernel = 0;   // 0: matrix-core kernel, 1: reference-grade fp32 kernel
   int32_t deterministic = 0;   // 1: fixed page range per split (no sharing between splits)
   int32_t write_evicts = 0;    // 1: a write that overflows a non-empty window evicts as it goes
+  int32_t out_bf16 = 0;        // 1: decode outputs are written as bf16
   bool has_rotation = false;
   // timing events per timed kernel: 2 * OSCAR_TIMING_PAIRS each when timing is on
   std::vector<hipEvent_t> timing_ev[2];
@@ -311,6 +312,7 @@ int launch_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, co
     a.n_split_max = static_cast<int32_t>(max_split);
     a.kernel = kv->decode_kernel;
     a.share = kv->deterministic ? 0 : 1;
+    a.out_bf16 = kv->out_bf16;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const auto [t0, t1] = kv->take_timing_pair(OSCAR_TIMED_DECODE);
     hipError_t e;
@@ -579,6 +581,12 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
       t0 += c;
     }
   }
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_output_bf16(oscar_kv* kv, int32_t on) {
+  if (!kv || (on != 0 && on != 1)) { set_error("oscar_kv_set_output_bf16: bad handle or value"); return OSCAR_E_ARG; }
+  kv->out_bf16 = on;
   return OSCAR_OK;
 }
 

@@ -234,6 +234,13 @@ int oscar_kv_set_rotation(oscar_kv *kv, const float *rot_host, void *stream);
 int oscar_kv_write(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, int32_t n_new,
                    const void *k, const void *v, void *stream);
 
+/* Output precision of oscar_decode_attn and oscar_decode_step: on = 1 writes
+ * `out` as bf16 (round to nearest even of the fp32 result; the pointer then
+ * addresses 2-byte elements, same [n_seqs][num_q_heads][128] order), on = 0
+ * (default) as fp32.  For engines whose output projection reads bf16.
+ * Errors: OSCAR_E_ARG. */
+int oscar_kv_set_output_bf16(oscar_kv *kv, int32_t on);
+
 /* Evicting writes (chunked prefill): on = 1 lets oscar_kv_write overflow a
  * non-empty sequence's window, evicting as it goes (see above); on = 0
  * (default) returns OSCAR_E_WINDOW_FULL instead.  Errors: OSCAR_E_ARG. */
@@ -276,7 +283,8 @@ int oscar_decode_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids, int
  * q         device bf16 [n_seqs][num_q_heads][128] (unrotated queries).
  * sm_scale  softmax scale (1/sqrt(128) for standard attention).
  * out       device fp32 [n_seqs][num_q_heads][128], softmax(sm_scale q k^T) v in
- *           the R_V basis.
+ *           the R_V basis (bf16 [n_seqs][num_q_heads][128] when
+ *           oscar_kv_set_output_bf16 is on).
  * ws        device workspace of at least oscar_decode_workspace_bytes bytes.
  * Errors: OSCAR_E_ARG, OSCAR_E_STATE (an empty sequence), OSCAR_E_WORKSPACE.
  */

@@ -376,6 +376,37 @@ def test_more_sequences_than_one_launch(gpu_lib):
     assert parity.rel_l2(out, ref) <= E2E_TOL
 
 
+@pytest.mark.parametrize("kernel", [0, 1])
+def test_bf16_output_is_rounded_fp32_output(gpu_lib, kernel):
+    """With bf16 output on, decode and the one-call step write exactly the round-to-nearest-even
+    bf16 of the fp32 output (deterministic mode, identical state)."""
+    import torch
+    hkv, hq = 2, 8
+    _case(f"bf16 output, kernel {kernel}")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 8, hkv)
+    ids = [1, 0, 2]
+    lengths = {0: 700, 1: 40, 2: 320 + 64 * 5}
+    sts = [_store(gpu_lib, hq, hkv, 3, 16, 40, None, rot) for _ in range(2)]
+    for st in sts:
+        st.set_decode_kernel(kernel)
+        st.set_decode_deterministic(True)
+    sts[1].set_output_bf16(True)
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, [0, 1, 2], hkv, max(lengths.values()) + 1)
+    for s_, L in lengths.items():
+        for st in sts:
+            st.write([s_], parity.to_dev_bf16(ks[s_:s_ + 1, :L]), parity.to_dev_bf16(vs[s_:s_ + 1, :L]))
+    q = parity.to_dev_bf16(synth.decode_queries(synth.CFG_QWEN3_4B, 8, 3, hq, hkv))
+    f32 = sts[0].decode(ids, q, SCALE)
+    b16 = sts[1].decode(ids, q, SCALE)
+    assert b16.dtype == torch.bfloat16
+    assert torch.equal(b16, f32.to(torch.bfloat16))
+    kt = parity.to_dev_bf16(np.stack([ks[s_, lengths[s_]] for s_ in ids]))
+    vt = parity.to_dev_bf16(np.stack([vs[s_, lengths[s_]] for s_ in ids]))
+    f32 = sts[0].decode_step(ids, kt, vt, q, SCALE)
+    b16 = sts[1].decode_step(ids, kt, vt, q, SCALE)
+    assert torch.equal(b16, f32.to(torch.bfloat16))
+
+
 def test_evicting_write_matches_token_by_token(gpu_lib):
     """Chunked prefill: a write that overflows a non-empty window, with evicting writes on, leaves
     pool, ring and page table bit-identical to writing the same tokens one at a time through the

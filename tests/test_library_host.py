@@ -157,6 +157,20 @@ def test_evicting_write_plan_matches_oracle():
     assert [s.seq_info(q) for q in range(3)] == snap[2]
 
 
+def test_switch_setters_reject_bad_values():
+    s = _plan_store()
+    for fn in ("oscar_kv_set_output_bf16", "oscar_kv_set_write_evicts"):
+        for bad in (-1, 2):
+            with pytest.raises(oscar.OscarError) as e:
+                oscar._check(getattr(oscar.load(), fn)(s.handle, bad))
+            assert e.value.status == oscar.E_ARG
+        with pytest.raises(oscar.OscarError) as e:
+            oscar._check(getattr(oscar.load(), fn)(None, 1))
+        assert e.value.status == oscar.E_ARG
+    s.set_output_bf16(True)
+    s.set_output_bf16(False)
+
+
 def test_decode_step_plan_and_errors():
     """The one-call decode step advances the host state exactly as the decode-step write, sizes its
     workspace for the state after that write, and changes nothing when it fails."""
