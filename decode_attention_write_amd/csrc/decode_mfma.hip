@@ -162,13 +162,15 @@ __device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl) {
 template <int G>
 __global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) { qprep_block<G>(a, blockIdx.x, blockIdx.y); }
 
-// The decode step's write and the query preparation in one launch: both work per (KV head,
-// sequence) and read that head's R_K.  The write lands in the ring before the split kernel,
-// which runs after this launch on the same stream, reads it (the new token attends to itself).
+// The decode step's write and the query preparation in one launch: grid (KV heads, sequences,
+// 2), z = 0 the write of one (KV head, sequence), z = 1 its query preparation.  The two touch
+// disjoint memory (ring and pool; query, workspace), so they run side by side.  The write lands
+// in the ring before the split kernel, which runs after this launch on the same stream, reads it
+// (the new token attends to itself).
 template <int G>
 __global__ __launch_bounds__(256) void k_step_qprep(StepArgs w, DecodeArgs a) {
-  step_write_block(w, blockIdx.x, blockIdx.y);
-  qprep_block<G>(a, blockIdx.x, blockIdx.y);
+  if (blockIdx.z == 0) step_write_block(w, blockIdx.x, blockIdx.y);
+  else qprep_block<G>(a, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -754,7 +756,7 @@ int decode_resident_workgroups(int gqa, int kernel) {
 
 template <int G>
 static hipError_t launch_g(const StepArgs* w, const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  if (w) hipLaunchKernelGGL(k_step_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, *w, a);
+  if (w) hipLaunchKernelGGL(k_step_qprep<G>, dim3(a.hkv, a.n_seqs, 2), dim3(256), 0, s, *w, a);
   else hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
   if (t0) {
     const hipError_t e = hipEventRecord(t0, s);
