@@ -1,5 +1,6 @@
 """How much the key rotation buys: INT2 logit error under the calibrated rotation, a Hadamard-only
-rotation and no rotation, on the oracle and on the library.
+rotation, a grouped (64-point, per quantizer group) Hadamard with the bit reversal after or before
+it, and no rotation, on the oracle and on the library.
 
 The pages credit the rotation for making INT2 keys usable: keys are rotated by R_K = U_Q H P_br
 before the 2-bit quantizer so that outlier channels no longer set the group ranges (axbrief,
@@ -13,7 +14,10 @@ On the synthetic keys (per-channel offsets N(0, 0.5^2), four outlier channels x2
 rotations cut the error several-fold against no rotation; the calibrated rotation is *not* better
 than Hadamard-only here, because the synthetic outliers sit on coordinate axes, which the
 Hadamard factor alone already spreads evenly, while the pages' gains come from real activations.
-Which rotation wins on real models is parity unpinned (no weights or activations here).
+Which rotation wins on real models is parity unpinned (no weights or activations here).  Under
+the grouped reading the order of the factors matters once the outliers crowd one group (here all
+four sit in channels 64-127): bit reversal before the grouped Hadamard moves half of the channels
+of each group into the other one, which evens the groups' ranges; after it, it does not.
 
 Also here: subtracting a key mean from every key shifts every score of a query by the same
 constant, which the softmax ignores (the OptR observation, gist.science summary of OptR, solution
@@ -35,8 +39,15 @@ STEPS = 8               # decode query draws
 
 
 def _rotations(r_k):
-    hp = calibration.sylvester_hadamard(D) @ calibration.bit_reversal_matrix(D)
+    pbr = calibration.bit_reversal_matrix(D)
+    hp = calibration.sylvester_hadamard(D) @ pbr
+    # the grouped reading: a 64-point Hadamard within each quantizer group (block diagonal), with
+    # the bit reversal after it (as written) or before it (mixing channels across the groups)
+    h64 = np.zeros((D, D))
+    h64[:64, :64] = h64[64:, 64:] = calibration.sylvester_hadamard(64)
     return {"calibrated": np.asarray(r_k, dtype=np.float32), "hadamard": hp.astype(np.float32),
+            "grouped_h64_then_pbr": (h64 @ pbr).astype(np.float32),
+            "pbr_then_grouped_h64": (pbr @ h64).astype(np.float32),
             "none": np.eye(D, dtype=np.float32)}
 
 
@@ -72,15 +83,18 @@ def _oracle_errors(rots, kb, vb, qs):
 
 
 def test_oracle_rotation_reduces_int2_logit_error():
-    """Both rotations cut the INT2 score error at least threefold against no rotation (measured:
-    calibrated 0.32, Hadamard-only 0.28, none 0.84 on these keys)."""
+    """Every rotation cuts the INT2 score error at least twofold against no rotation (measured:
+    calibrated 0.32, Hadamard-only 0.28, grouped Hadamard then bit reversal 0.40, bit reversal then
+    grouped Hadamard 0.26, none 0.84 on these keys, whose four outlier channels all sit in the
+    second 64-channel group)."""
     kb, vb, qs = _inputs()
     q_cal = synth.bf16_bits_to_f32(synth.calibration_queries(synth.CFG_TINY, 0, 0)).astype(np.float64)
     r_k, _ = calibration.key_rotation(q_cal)
     e = _oracle_errors(_rotations(r_k), kb, vb, qs)
     print("oracle INT2 logit rel. error:", {k: round(v, 4) for k, v in e.items()})
-    assert e["none"] > 2.5 * e["calibrated"] and e["none"] > 2.5 * e["hadamard"], e
-    assert 0.05 < e["hadamard"] < 0.6 and 0.05 < e["calibrated"] < 0.6, e
+    for name, v in e.items():
+        if name != "none":
+            assert 0.05 < v < 0.6 and e["none"] > 2 * v, (name, e)
 
 
 def test_key_mean_subtraction_is_attention_exact():
@@ -100,10 +114,10 @@ def test_key_mean_subtraction_is_attention_exact():
 @pytest.mark.gpu
 def test_gpu_rotation_quality_matches_oracle(gpu_lib):
     """The library's INT2 state gives the oracle's score error for each rotation (within 3 %),
-    and the same ordering: no rotation at least 2.5x worse than either rotation."""
+    and no rotation is at least twice as bad as any rotation."""
     import parity
 
-    print("[case] rotation quality: calibrated / Hadamard-only / none, 2048 tokens", flush=True)
+    print("[case] rotation quality: calibrated / Hadamard-only / grouped Hadamard / none, 2048 tokens", flush=True)
     kb, vb, qs = _inputs()
     r_k = parity.calibrate(synth.CFG_TINY, 0, HKV)[0]
     rots = _rotations(r_k)
@@ -119,4 +133,6 @@ def test_gpu_rotation_quality_matches_oracle(gpu_lib):
     print("library INT2 logit rel. error:", {k: round(v, 4) for k, v in got.items()}, flush=True)
     for name in rots:
         assert abs(got[name] - want[name]) <= 0.03 * want[name], (name, got[name], want[name])
-    assert got["none"] > 2.5 * got["calibrated"] and got["none"] > 2.5 * got["hadamard"], got
+    for name, v in got.items():
+        if name != "none":
+            assert got["none"] > 2 * v, (name, got)
