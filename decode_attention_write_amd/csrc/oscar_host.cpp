@@ -146,7 +146,29 @@ int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd
   return OSCAR_OK;
 }
 
-int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
+// (length, INT2 count) of each listed sequence, in list order: the state a decode call plans for
+struct SeqState {
+  int64_t len, n2;
+};
+
+std::vector<SeqState> current_state(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
+  std::vector<SeqState> st(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) st[i] = SeqState{kv->len[seq_ids[i]], kv->n_int2[seq_ids[i]]};
+  return st;
+}
+
+// The state after a decode-step write: one more token per sequence, and one more INT2 token
+// where the window is full.
+std::vector<SeqState> state_after_step(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs) {
+  std::vector<SeqState> st = current_state(kv, seq_ids, n_seqs);
+  for (SeqState& q : st) {
+    if (q.len > 0 && std::max<int64_t>(0, q.len - kSink - q.n2) == kWin) q.n2 += 1;
+    q.len += 1;
+  }
+  return st;
+}
+
+int64_t choose_pages_per_split(const oscar_kv* kv, int32_t n_seqs, const std::vector<SeqState>& st) {
   if (kv->pages_per_split > 0) return kv->pages_per_split;
   // Work-groups of the split kernel that fit on the device at once (the matrix-core kernel uses
   // one wavefront per work-group).  Aim for a single residency round holding as many waves as
@@ -162,7 +184,7 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
     const int n = std::min(CHUNK, n_seqs - c0);
     int64_t max_pages = 0, total = 0;
     for (int i = c0; i < c0 + n; ++i) {
-      const int64_t p = ceil_div(kv->n_int2[seq_ids[i]], kPage);
+      const int64_t p = ceil_div(st[i].n2, kPage);
       max_pages = std::max(max_pages, p);
       total += p;
     }
@@ -170,10 +192,8 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
     const int kernel = kv->decode_kernel;
     auto wgs_for = [&](int64_t pps) {
       int64_t w = 0;
-      for (int i = c0; i < c0 + n; ++i) {
-        const int s = seq_ids[i];
-        w += unit_workgroups(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]), static_cast<int>(pps), kernel);
-      }
+      for (int i = c0; i < c0 + n; ++i)
+        w += unit_workgroups(static_cast<int>(st[i].n2), static_cast<int>(st[i].len), static_cast<int>(pps), kernel);
       return w * hkv;
     };
     const int64_t budget = std::max<int64_t>(n * hkv, resident);
@@ -190,6 +210,20 @@ int64_t choose_pages_per_split(const oscar_kv* kv, const int32_t* seq_ids, int32
 // token into INT2.
 int64_t overflow_evictions(const oscar_kv* kv, int s, int64_t n_new) {
   return std::max<int64_t>(0, n_new - (kRing - (kv->len[s] - kv->n_int2[s])));
+}
+
+// Workspace bytes of a decode call over sequences in state st: split partials, then the prepared
+// queries, then one page counter per split (matrix-core kernel).
+size_t workspace_bytes_for(const oscar_kv* kv, int32_t n_seqs, const std::vector<SeqState>& st) {
+  const int64_t pps = choose_pages_per_split(kv, n_seqs, st);
+  int64_t max_split = 1;
+  for (int i = 0; i < n_seqs; ++i)
+    max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(st[i].n2), static_cast<int>(st[i].len),
+                                                          static_cast<int>(pps), kv->decode_kernel));
+  const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
+  return static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float) +
+         static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE +
+         static_cast<size_t>(rows) * kv->desc.num_kv_heads * max_split * sizeof(int32_t);
 }
 
 // ---- decode-step write and decode attention, shared by the one-call and two-call forms
@@ -287,7 +321,7 @@ int check_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, con
 int launch_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const std::vector<StepSeq>* plan,
                   const void* q, float sm_scale, float* out, void* ws, hipStream_t st, const char* who,
                   const void* k = nullptr, const void* v = nullptr) {
-  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
+  const int64_t pps = choose_pages_per_split(kv, n_seqs, current_state(kv, seq_ids, n_seqs));
   for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
     DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -675,18 +709,7 @@ int oscar_decode_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids, int
   if (!kv || !bytes) { set_error("oscar_decode_workspace_bytes: null argument"); return OSCAR_E_ARG; }
   int rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
-  const int64_t pps = choose_pages_per_split(kv, seq_ids, n_seqs);
-  int64_t max_split = 1;
-  for (int i = 0; i < n_seqs; ++i) {
-    const int s = seq_ids[i];
-    max_split = std::max<int64_t>(max_split, unit_records(static_cast<int>(kv->n_int2[s]), static_cast<int>(kv->len[s]),
-                                                          static_cast<int>(pps), kv->decode_kernel));
-  }
-  const int64_t rows = std::min<int64_t>(n_seqs, CHUNK);
-  // split partials, then the prepared queries, then one page counter per split (matrix-core kernel)
-  *bytes = static_cast<size_t>(rows) * kv->desc.num_q_heads * max_split * PART_STRIDE * sizeof(float) +
-           static_cast<size_t>(rows) * kv->desc.num_kv_heads * QPREP_STRIDE +
-           static_cast<size_t>(rows) * kv->desc.num_kv_heads * max_split * sizeof(int32_t);
+  *bytes = workspace_bytes_for(kv, n_seqs, current_state(kv, seq_ids, n_seqs));
   return OSCAR_OK;
 }
 
@@ -709,23 +732,9 @@ int oscar_decode_step_workspace_bytes(const oscar_kv* kv, const int32_t* seq_ids
   if (!kv || !bytes) { set_error("oscar_decode_step_workspace_bytes: null argument"); return OSCAR_E_ARG; }
   int rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
-  // the attention runs on the state after the step's write: one more token per sequence, and
-  // one more INT2 token where the window is full.  The host mirror is advanced for the count and
-  // restored (a handle is used by one host thread at a time).
-  oscar_kv* m = const_cast<oscar_kv*>(kv);
-  std::vector<std::pair<int64_t, int64_t>> saved(n_seqs);
-  for (int i = 0; i < n_seqs; ++i) {
-    const int s = seq_ids[i];
-    saved[i] = {m->len[s], m->n_int2[s]};
-    if (m->len[s] > 0 && std::max<int64_t>(0, m->len[s] - kSink - m->n_int2[s]) == kWin) m->n_int2[s] += 1;
-    m->len[s] += 1;
-  }
-  rc = oscar_decode_workspace_bytes(kv, seq_ids, n_seqs, bytes);
-  for (int i = n_seqs - 1; i >= 0; --i) {
-    m->len[seq_ids[i]] = saved[i].first;
-    m->n_int2[seq_ids[i]] = saved[i].second;
-  }
-  return rc;
+  // the attention runs on the state after the step's write
+  *bytes = workspace_bytes_for(kv, n_seqs, state_after_step(kv, seq_ids, n_seqs));
+  return OSCAR_OK;
 }
 
 int oscar_decode_step(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
