@@ -254,7 +254,7 @@ def prefill_leg(reps=5):
     return res
 
 
-def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0):
+def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0, flush_mode="read"):
     """One attention layer over sequences of the given lengths (one R_K per KV head, pages in a
     seeded shuffled order): prefill writes, then `reps` decode steps (the decode-step write of
     one token per sequence, then decode attention), each after one untimed step.  Returns the
@@ -295,8 +295,11 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0):
     def step(i):
         st.decode_step(seqs, newk[i], newv[i], q, scale, out=out, ws=ws)
 
-    # the layer's cache may fit the 256 MB last-level cache: overwrite a larger buffer before
-    # every timed step so that each one reads its pages from HBM
+    # the layer's cache may fit the 256 MB last-level cache: stream a larger buffer through it
+    # before every timed step so that each one reads its pages from HBM.  The buffer is read, not
+    # written ("read"): a fill leaves up to 256 MB of dirty lines whose write-back then competes
+    # with the timed kernel's reads (measured: 8 x 32768 layer 51.9 -> 48.4 us, ragged GQA-8
+    # layer 223 -> 198 us, whose 763 MB cannot be served from the cache in either mode)
     flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
     st.set_timing(True)
     step(0)
@@ -304,8 +307,12 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0):
     st.read_timing(oscar.TIMED_DECODE)
     info = [st.seq_info(s) for s in seqs]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    flush.fill_(1)
     for i in range(reps):
-        flush.fill_(i)
+        if flush_mode == "write":
+            flush.fill_(i)
+        else:
+            flush.sum()
         evs[i][0].record()
         step(1 + i)
         evs[i][1].record()
@@ -356,6 +363,8 @@ def main():
     ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
     ap.add_argument("--layer-pps", type=int, default=0,
                     help="development: pages per decode split in the single-layer legs (0 = library choice)")
+    ap.add_argument("--layer-flush", choices=["write", "read"], default="read",
+                    help="development: how the single-layer legs push their cache out of the last-level cache")
     ap.add_argument("--two-call", action="store_true",
                     help="development: the decode-step write and the attention as two calls")
     ap.add_argument("--separate-write", action="store_true",
@@ -624,11 +633,12 @@ def main():
     if not args.no_layers:
         result["layer_qwen3_4b_32k_b8"] = layer_leg(
             synth.CFG_QWEN3_4B, 32, 8, [32768] * 8, 20,
-            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context", pps=args.layer_pps)
+            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context", pps=args.layer_pps,
+            flush_mode=args.layer_flush)
         result["layer_qwen3_32b_ragged_b16"] = layer_leg(
             synth.CFG_QWEN3_32B, 64, 8, [int(x) for x in synth.ragged_lengths(synth.CFG_QWEN3_32B, 16, 8192, 131072)],
             20, "qwen3-32b-shaped layer: 64 q / 8 kv heads (GQA 8), batch 16, lengths U[8192, 131072]",
-            pps=args.layer_pps)
+            pps=args.layer_pps, flush_mode=args.layer_flush)
     if args.copy_calib_mib:
         # a plain copy of known size, for scaling the memory counters of a profiled run
         n = args.copy_calib_mib * (1 << 20) // 4
