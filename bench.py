@@ -371,8 +371,8 @@ def main():
                     help="write each step with the eviction and the append as two calls (comparison)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the decode step shards by sequence or KV head with no exchange; see DESIGN.md).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the decode step shards by sequence or KV head with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

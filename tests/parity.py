@@ -1,4 +1,4 @@
-"""Helpers for GPU-vs-oracle parity: store export, judge rules, workload set-up."""
+"""Helpers for GPU-vs-oracle parity: store export, tolerance rules, workload set-up."""
 from __future__ import annotations
 
 import numpy as np
@@ -35,7 +35,7 @@ def calibrate(cfg, layer, hkv):
     return np.stack(rots)
 
 
-# ----------------------------------------------------------------------------- judge rules
+# ----------------------------------------------------------------------------- tolerance rules
 
 class Report(dict):
     pass

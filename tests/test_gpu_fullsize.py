@@ -3,7 +3,7 @@
 Inputs are drawn on the GPU by the counter-based generator; the oracle side redraws the
 sampled units' inputs with the CPU twin (bit-identical).  The decode check runs the oracle on
 the GPU's exported store (identical state); the write check compares the sampled units' INT2
-pages, ring slots and the page table under the judge rules.
+pages, ring slots and the page table under the tolerance rules.
 """
 import math
 

@@ -14,7 +14,7 @@ from oracle import attention, store as ostore
 pytestmark = pytest.mark.gpu
 D = 128
 SCALE = 1.0 / math.sqrt(D)
-# Decode parity is judged on identical cache state (oracle run on the GPU's exported store):
+# Decode parity is checked on identical cache state (oracle run on the GPU's exported store):
 # rel-L2 <= 1e-3.  End to end (each side on its own store) the outputs also differ by the write
 # path's allowed rounding: fp32 rotation vs the oracle's fp64 product flips a few codes that lie
 # within 1e-3 * scale of a rounding boundary, each moving one key element by a full quantization
@@ -74,7 +74,7 @@ def _bf16_ulp(x):
 
 def _check_state(gpu, ora, seqs, rot, inputs):
     """Page tables exact; ring V bit-exact, ring K within the fp32 rotation error bound; INT2 pages
-    written by the first (prefill) write under the judge rules.
+    written by the first (prefill) write under the tolerance rules.
 
     inputs[s] = (k_bits [n, Hkv, 128], v_bits, prefill_len): every token written to sequence s so far.
     """
@@ -310,7 +310,7 @@ def test_degenerate_and_extreme_groups(gpu_lib):
     """Quantizer edge cases through the whole path with an identity rotation (both sides quantize
     identical fp32 inputs): constant and all-zero groups, scales that underflow fp16 (every code 0),
     fp16-denormal scales, one-signed groups far from zero and groups near the fp16 limit; stored
-    state under the judge rules with no metadata flip, then evictions of such tokens and decode
+    state under the tolerance rules with no metadata flip, then evictions of such tokens and decode
     parity on identical state, with finite outputs."""
     hkv, hq, L = 1, 2, 320 + 64 * 3 + 17
     _case("degenerate / extreme quantizer groups, identity rotation")
