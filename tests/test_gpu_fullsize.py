@@ -119,6 +119,63 @@ def test_qwen3_4b_full_context(gpu_lib):
         assert err <= 1e-3
 
 
+def test_qwen3_8b_layer_100k_b32(gpu_lib):
+    """One layer of the 36-layer Qwen3-8B-shaped step at full size (32 q / 8 kv heads, batch 32,
+    100000-token context, shuffled physical pages), in the launch configuration the benchmark
+    times: one-call decode steps (write + attention).  Page table exact; sampled units' INT2
+    pages, evicted tokens and decode outputs against the oracle."""
+    import torch
+    from synth import gpu as sg
+    cfg, hkv, hq, B, L = synth.CFG_QWEN3_8B, 8, 32, 32, 100000
+    _case("qwen3-8b layer full: 32 x 100000, one-call decode step")
+    rot = parity.calibrate(cfg, 0, hkv)
+    max_pages = -(-(L + 2) // 64) + 1
+    num_pages = B * max_pages
+    free = synth.page_permutation(cfg, 0, num_pages)
+    st = gpu_lib.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=free)
+    poison(st)
+    st.set_rotation(rot)
+    prm = sg.HeadParams(cfg, 0, hkv)
+    kbuf = torch.empty((1, L + 2, hkv, D), dtype=torch.int16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    newk = torch.empty((2, B, hkv, D), dtype=torch.int16, device="cuda")
+    newv = torch.empty_like(newk)
+    for s in range(B):
+        sg.draw_kv(prm, s, 0, L + 2, kbuf[0], vbuf[0])
+        st.write([s], kbuf[:, :L], vbuf[:, :L])
+        newk[:, s] = kbuf[0, L:L + 2]
+        newv[:, s] = vbuf[0, L:L + 2]
+    del kbuf, vbuf
+    seqs = list(range(B))
+    q = synth.decode_queries(cfg, 0, B, hq, hkv)
+    qd = parity.to_dev_bf16(q)
+    before = parity.export(st)
+    st.decode_step(seqs, newk[0], newv[0], qd, SCALE)            # evicts INT2 index L-320, appends
+    gpu = parity.export(st)
+    out = st.decode_step(seqs, newk[1], newv[1], qd, SCALE).cpu().numpy()
+    after = parity.export(st)
+    # allocator: one write per sequence in order, then the steps' evictions (index L-320 starts
+    # no page: (L-320) % 64 = 32)
+    ora_t = _oracle_table([L] * B, max_pages, num_pages, free)
+    assert np.array_equal(after[2], ora_t)
+    for s, kv in [(0, 0), (19, 5)]:
+        _check_write_unit(gpu, cfg, 0, s, kv, L, rot, gpu[2][s], L - 320 + 1)
+        kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(before[1], s, L - 320)
+        blk = layout.unpack_head_block(gpu[0][gpu[2][s, (L - 320) // 64], kv])
+        j = (L - 320) % 64
+        assert np.array_equal(blk[0][j], kc[kv]) and np.array_equal(blk[1][j], vc[kv])
+        assert np.array_equal(blk[2][j], ksc[kv]) and np.array_equal(blk[3][j], klo[kv])
+        assert np.array_equal(blk[4][j], vsc[kv]) and np.array_equal(blk[5][j], vlo[kv])
+    lens = np.full(B, L + 2)
+    n2s = np.full(B, L - 320 + 2)
+    g = hq // hkv
+    for s, kv in [(0, 0), (19, 5), (31, 7)]:
+        iso = _iso_decode_unit(after, lens, n2s, rot, q, s, kv, g)
+        err = parity.rel_l2(out[s, kv * g:(kv + 1) * g], iso)
+        print(f"[parity] decode unit seq={s} kv={kv} rel-l2 {err:.2e}", flush=True)
+        assert err <= 1e-3
+
+
 def test_prefill_131072_then_1024_appends(gpu_lib):
     """One 131072-token sequence x 8 KV heads, then 1024 decode-step writes (evict 1 + append 1 each)."""
     import torch
