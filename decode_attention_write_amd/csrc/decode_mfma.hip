@@ -63,7 +63,7 @@ __host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
 // page, and the BF16 sink + window work when it is folded, belong to split 0 and are done
 // before its page loop.
 template <int G>
-__host__ __device__ constexpr int share_group() { return G == 8 ? 2 : 3; }
+__host__ __device__ constexpr int share_group() { return 3; }
 
 // Per (sequence of the chunk, KV head): one page counter per split.
 __host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
@@ -629,54 +629,33 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   group_ids(n_first, n_n, n0, n1, n2);
 
   {
-    // NB rotating register sets: NB - 1 pages in flight while one is processed (two for
-    // GQA <= 4; one for GQA 8, whose registers are taken by its wider P.V operands).  One step
-    // processes the current group t and loads the next group n; the loop has a single exit.
+    // Three rotating register sets: two pages in flight while one is processed (GQA 8 too: at its
+    // 2 waves per SIMD the third set fits the register budget; with one page in flight it was
+    // 1.4 % slower).  One step processes the current group t and loads the next group n; the
+    // loop has a single exit.
     const std::true_type full{};
-    if constexpr (NB == 2) {
-      Raw b0, b1;
-      load_block(t0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t_n > 0) {
-        do {
-          load_block(t1, b1);
-          claim();  // after the load: processing b0 then waits for b0 only
-          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
-          process_page(0, b0, full);
-          load_block(n0, b0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (t_n > 1) process_page(0, b1, full);
-          t_n = n_n;
-          t0 = n0;
-          t1 = n1;
-          resolve(n_first, n_n);
-          group_ids(n_first, n_n, n0, n1, n2);
-        } while (t_n > 0);
-      }
-    } else {
-      Raw b0, b1, b2;
-      load_block(t0, b0);
-      __builtin_amdgcn_sched_barrier(0);  // keep page order in the queue: waits stay vmcnt(10)
-      load_block(t1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t_n > 0) {
-        do {
-          claim();
-          load_block(t2, b2);
-          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
-          process_page(0, b0, full);
-          load_block(n0, b0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (t_n > 1) process_page(0, b1, full);
-          load_block(n1, b1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (t_n > 2) process_page(0, b2, full);
-          t_n = n_n;
-          t2 = n2;
-          resolve(n_first, n_n);
-          group_ids(n_first, n_n, n0, n1, n2);
-        } while (t_n > 0);
-      }
+    Raw b0, b1, b2;
+    load_block(t0, b0);
+    __builtin_amdgcn_sched_barrier(0);  // keep page order in the queue: waits stay vmcnt(10)
+    load_block(t1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t_n > 0) {
+      do {
+        claim();
+        load_block(t2, b2);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the page's math
+        process_page(0, b0, full);
+        load_block(n0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t_n > 1) process_page(0, b1, full);
+        load_block(n1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t_n > 2) process_page(0, b2, full);
+        t_n = n_n;
+        t2 = n2;
+        resolve(n_first, n_n);
+        group_ids(n_first, n_n, n0, n1, n2);
+      } while (t_n > 0);
     }
   }
 
