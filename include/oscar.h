@@ -306,8 +306,11 @@ int oscar_decode_step_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids
  * one fused pass; the write shares the launch of the query preparation).
  * k, v      device bf16 [n_seqs][num_kv_heads][128], row i for seq_ids[i].
  * q         device bf16 [n_seqs][num_q_heads][128] (unrotated queries).
- * out       device fp32 [n_seqs][num_q_heads][128], in the R_V basis.
+ * sm_scale  softmax scale (1/sqrt(128) for standard attention).
+ * out       device fp32 [n_seqs][num_q_heads][128], in the R_V basis (bf16 when
+ *           oscar_kv_set_output_bf16 is on).
  * ws        device workspace of at least oscar_decode_step_workspace_bytes bytes.
+ * The caller owns every buffer; calls are enqueued on stream in order.
  * Errors: OSCAR_E_ARG, OSCAR_E_STATE (an empty sequence, or no rotation),
  * OSCAR_E_NOPAGE, OSCAR_E_WORKSPACE; nothing is changed on error.
  */
