@@ -131,3 +131,31 @@ def unpack_head_block(blk, n_tokens: int = PAGE_TOKENS):
     vc = _unpack_area(blk[V_CODES_OFF:V_CODES_OFF + 2048], n_tokens, v_code_position)
     meta = blk[META_OFF:].view(np.float16).reshape(PAGE_TOKENS, 8)[:n_tokens]
     return kc, vc, meta[:, [0, 2]], meta[:, [1, 3]], meta[:, [4, 6]], meta[:, [5, 7]]
+
+
+_GRID = {}
+
+
+def _grid(position):
+    """(word, bit) of every (token, channel) of a full page for one code area, computed once."""
+    if position not in _GRID:
+        jj, cc = np.meshgrid(np.arange(PAGE_TOKENS), np.arange(HEAD_DIM), indexing="ij")
+        word, bit = position(jj, cc)
+        _GRID[position] = (np.asarray(word), np.asarray(bit).astype(np.uint32))
+    return _GRID[position]
+
+
+def unpack_pages(blocks):
+    """``unpack_head_block`` of many full page blocks at once (blocks uint8 [P, 5120]).
+
+    Returns k_codes, v_codes (uint8 [P, 64, 128]) and k_s16, k_lo16, v_s16, v_lo16
+    (float16 [P, 64, 2]); tokens past a partially filled page's count come out as stored (zero).
+    """
+    blocks = np.ascontiguousarray(np.asarray(blocks, dtype=np.uint8)).reshape(-1, HEAD_BLOCK)
+    out = []
+    for off, position in ((K_CODES_OFF, k_code_position), (V_CODES_OFF, v_code_position)):
+        words = blocks[:, off:off + 2048].view(np.uint32)          # [P, 512]
+        word, bit = _grid(position)
+        out.append(((words[:, word] >> bit) & np.uint32(3)).astype(np.uint8))
+    meta = blocks[:, META_OFF:].view(np.float16).reshape(-1, PAGE_TOKENS, 8)
+    return (out[0], out[1], meta[..., [0, 2]], meta[..., [1, 3]], meta[..., [4, 6]], meta[..., [5, 7]])

@@ -6,22 +6,27 @@ path each (rotated) token is clipped with the calibrated thresholds c_K = 0.96
 asymmetrically, to INT2 in groups of G_K = 64 channels.  INT2 has four levels
 (axbrief introduction; gist section "문제점").
 
-Readings taken where the pages are silent (each step below is one IEEE fp32
-operation, round to nearest even, never fused):
+Readings taken where the pages are silent (steps 2-6 are each one IEEE fp32
+operation, round to nearest even, never fused; the stored metadata must come
+out bit for bit the same from any implementation of the same sequence):
 1. mn, mx = min and max of the 64 values of the group (exact).
 2. r  = mx - mn
 3. w  = c * r                      (clipped width: the range shrinks to c*r)
 4. lo = mn + 0.5 * (r - w)         (trim (1-c)/2 of the range from each end)
 5. s  = w / 3                      (correctly rounded division; 4 levels)
 6. s16 = fp16(s), lo16 = fp16(lo)  (stored metadata, round to nearest even)
-7. if s16 == 0 every code is 0; else inv = fp32(1 / s16),
-   t = fp32(fp32(x - lo16) * inv), code = clamp(round_half_even(t), 0, 3).
-   The pages fix no precision for this decision, so it is taken in the
-   kernel's precision (fp32), the same sequence on both sides.
+7. if s16 == 0 every code is 0; else t = (x - lo16) / s16 in fp64 and
+   code = clamp(round_half_even(t), 0, 3).
 Dequantized value: lo16 + s16 * code.
 
+The code decision in step 7 is exact (fp64 of fp32/fp16 operands); an
+implementation that takes it in fp32 can differ only where t lies within a few
+fp32 ulps of a rounding boundary b in {0.5, 1.5, 2.5}.  ``boundary_distance``
+measures |t - b| for the parity rule that tolerates such elements.
+
 Parity: pinned (hand-worked golden groups, four-level range, brute-force
-nearest level, error bound, clipping width and midpoint).
+nearest level, error bound, clipping width and midpoint, boundary distances of
+hand-placed values).
 """
 from __future__ import annotations
 
@@ -32,10 +37,11 @@ C_K = np.float32(0.96)
 C_V = np.float32(0.92)
 
 
-def quantize(x, c):
-    """Quantize float32 rows ``x[..., 128]``.
+def params(x, c):
+    """Steps 1-6 for float32 rows ``x[..., 128]``, per 64-channel group.
 
-    Returns (codes uint8 [..., 128], s16 float16 [..., n_groups], lo16 float16 [..., n_groups]).
+    Returns (s32, lo32, s16, lo16): the fp32 scale and minimum before the fp16
+    rounding, and the stored fp16 values; each [..., n_groups].
     """
     x = np.asarray(x, dtype=np.float32)
     c = np.float32(c)
@@ -49,17 +55,24 @@ def quantize(x, c):
     half = (np.float32(0.5) * (r - w).astype(np.float32)).astype(np.float32)
     lo32 = (mn + half).astype(np.float32)
     s32 = (w / np.float32(3.0)).astype(np.float32)
-    s16 = s32.astype(np.float16)
-    lo16 = lo32.astype(np.float16)
-    s_f = s16.astype(np.float32)
-    lo_f = lo16.astype(np.float32)
+    return s32, lo32, s32.astype(np.float16), lo32.astype(np.float16)
+
+
+def quantize(x, c):
+    """Quantize float32 rows ``x[..., 128]``.
+
+    Returns (codes uint8 [..., 128], s16 float16 [..., n_groups], lo16 float16 [..., n_groups]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    _, _, s16, lo16 = params(x, c)
+    xg = x.reshape(x.shape[:-1] + (d // GROUP, GROUP)).astype(np.float64)
+    s = s16.astype(np.float64)[..., None]
+    lo = lo16.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        inv = np.where(s_f != 0, np.float32(1.0) / np.where(s_f != 0, s_f, np.float32(1.0)),
-                       np.float32(0.0)).astype(np.float32)
-    diff = (xg - lo_f[..., None]).astype(np.float32)
-    t = (diff * inv[..., None]).astype(np.float32)
-    codes = np.clip(np.rint(t), 0, 3).astype(np.uint8)
-    codes = np.where((s_f != 0)[..., None], codes, np.uint8(0))
+        t = (xg - lo) / np.where(s != 0, s, 1.0)
+    codes = np.clip(np.rint(t), 0, 3).astype(np.uint8)     # np.rint: round half to even
+    codes = np.where(s != 0, codes, np.uint8(0))
     return codes.reshape(x.shape), s16, lo16
 
 
@@ -73,7 +86,8 @@ def dequantize(codes, s16, lo16) -> np.ndarray:
 
 
 def boundary_distance(x, s16, lo16) -> np.ndarray:
-    """|t - b| in fp64 for the nearest rounding boundary b in {0.5, 1.5, 2.5}, per element.
+    """|t - b| in fp64 for the nearest rounding boundary b in {0.5, 1.5, 2.5}, per element,
+    with t = (x - lo16) / s16.
 
     Used by the parity rule: a code mismatch is explained when the value lies within
     1e-3 * s16 of a boundary.  Groups with s16 == 0 give +inf.

@@ -510,3 +510,114 @@ def test_value_rotation_and_fold_are_output_exact():
         ref += o @ w_o[j * D:(j + 1) * D]
         got += o2 @ w_o2[j * D:(j + 1) * D]
     assert np.abs(got - ref).max() < 1e-10 * np.abs(ref).max()
+
+
+# ----------------------------------------------------------------------------- code decision and the
+# parity band
+
+def _group_with(s_target, lo_target, ts):
+    """A 64-value group whose clipped range gives fp32 parameters near (s_target, lo_target) under
+    c_K, with the listed values placed at t = (x - lo16) / s16 (filled up with t = 1)."""
+    # mn, mx such that c r = 3 s and mn + (r - c r) / 2 = lo: r = 3 s / c, mn = lo - (1 - c) r / 2
+    c = float(quantizer.C_K)
+    r = 3.0 * s_target / c
+    mn = lo_target - 0.5 * (1.0 - c) * r
+    x = np.full(64, mn, np.float32)
+    x[1] = np.float32(mn + r)
+    _, _, s16, lo16 = quantizer.params(np.concatenate([x, x])[None], quantizer.C_K)
+    s, lo = float(s16[0, 0]), float(lo16[0, 0])
+    vals = np.array([lo + t * s for t in ts], np.float64)
+    assert np.all(vals.astype(np.float32).astype(np.float64) == vals), "placed values must be exact in fp32"
+    x[2:2 + len(ts)] = vals.astype(np.float32)
+    x[2 + len(ts):] = np.float32(lo + s)
+    row = np.concatenate([x, x])[None]
+    return row, s, lo
+
+
+def test_code_decision_ties_and_boundary_distance():
+    """Hand-placed values around each rounding boundary b in {0.5, 1.5, 2.5}: the code is the
+    exact fp64 decision with ties to even, and boundary_distance returns the placement offset.
+    Scale and minimum: s16 = 1, lo16 = -1 exactly (r = 3.125, c_K: w = 3, half = 1/16), and a
+    second group whose fp32 scale 0.9921875... is not an fp16 number, so that a distance or a code
+    taken with the fp32 parameters instead of the stored fp16 ones fails."""
+    want = [0, 2, 2, 1, 1, 3, 2, 0, 3, 1]
+    # offsets small enough to be exact in fp32 with each group's fp16 scale
+    for s_t, lo_t, d in ((1.0, -1.0, 2.0 ** -16), (0.99, 0.37, 2.0 ** -9)):
+        ts = [0.5, 1.5, 2.5, 0.5 + d, 1.5 - d, 2.5 + d, 2.5 - d, 0.0, 3.0, 1.25]
+        want_dist = [0, 0, 0, d, d, d, d, 0.5, 0.5, 0.25]
+        row, s, lo = _group_with(s_t, lo_t, ts)
+        s32, lo32, s16, lo16 = quantizer.params(row, quantizer.C_K)
+        if s_t == 1.0:
+            assert (s, lo) == (1.0, -1.0) and float(s32[0, 0]) == 1.0 and float(lo32[0, 0]) == -1.0
+        else:
+            assert float(s32[0, 0]) != s       # the stored scale differs from the fp32 one
+        codes, _, _ = quantizer.quantize(row, quantizer.C_K)
+        assert list(codes[0, 2:2 + len(ts)]) == want, (s_t, codes[0, 2:2 + len(ts)])
+        dist = quantizer.boundary_distance(row, s16, lo16)[0, 2:2 + len(ts)]
+        assert np.abs(dist - np.array(want_dist)).max() < 1e-12, dist
+    # a group whose scale rounds to fp16 zero: distance +inf, every code 0
+    tiny = np.full((1, D), 1.0, np.float32)
+    tiny[0, :64:2] += np.float32(1e-8)
+    c0, s0, l0 = quantizer.quantize(tiny, quantizer.C_K)
+    assert float(s0[0, 0]) == 0 and (c0 == 0).all()
+    assert np.isinf(quantizer.boundary_distance(tiny, s0, l0)[0, :64]).all()
+
+
+def test_store_partial_last_page_decode_by_hand():
+    """A store holding 64 sink + 145 INT2 (two full pages and a 17-token page, shuffled physical
+    pages) + 256 window tokens, decoded by the oracle, against a hand-built cache: each position
+    routed by its index, INT2 tokens dequantized element by element as lo16 + s16 * code from the
+    quantizer's output on fp32(k R) (values on v), BF16 tokens from bf16(k R) / v, and attention
+    by pure-Python loops."""
+    import math
+    hkv, hq, L = 2, 4, 320 + 2 * 64 + 17
+    rot = _rot(hkv)
+    kb = np.stack([synth.unit_kv(synth.CFG_TINY, 0, 3, kv, L)[0] for kv in range(hkv)], axis=1)
+    vb = np.stack([synth.unit_kv(synth.CFG_TINY, 0, 3, kv, L)[1] for kv in range(hkv)], axis=1)
+    free = [5, 2, 7, 0, 3, 6, 1, 4]
+    st = store.OracleStore(hkv, 2, 4, 8, free, rot)
+    st.write([1], kb[None], vb[None])
+    assert st.n_int2[1] == 145 and list(st.page_table[1, :3]) == [5, 2, 7]
+    qb = synth.decode_queries(synth.CFG_TINY, 0, 1, hq, hkv)
+    out = attention.decode_store(st, qb, [1], 1 / math.sqrt(D), hq)
+    q = synth.bf16_bits_to_f32(qb).astype(np.float64)[0]
+    g = hq // hkv
+    for kv in range(hkv):
+        k = synth.bf16_bits_to_f32(kb[:, kv]).astype(np.float64)
+        v = synth.bf16_bits_to_f32(vb[:, kv]).astype(np.float64)
+        x = k @ rot[kv].astype(np.float64)
+        kc, ks, kl = quantizer.quantize(x[64:209].astype(np.float32), quantizer.C_K)
+        vc, vs, vl = quantizer.quantize(v[64:209].astype(np.float32), quantizer.C_V)
+        keys, vals = [], []
+        for p in range(L):
+            if 64 <= p < 209:
+                i = p - 64
+                keys.append([float(kl[i, c // 64]) + float(ks[i, c // 64]) * int(kc[i, c]) for c in range(D)])
+                vals.append([float(vl[i, c // 64]) + float(vs[i, c // 64]) * int(vc[i, c]) for c in range(D)])
+            else:
+                keys.append(list(store.bf16_to_f64(store.to_bf16_bits_f64(x[p]))))
+                vals.append(list(v[p]))
+        for h in range(kv * g, (kv + 1) * g):
+            qr = list(q[h] @ rot[kv].astype(np.float64))
+            scores = [sum(a * b for a, b in zip(qr, kk)) / math.sqrt(D) for kk in keys]
+            m = max(scores)
+            e = [math.exp(s_ - m) for s_ in scores]
+            tot = sum(e)
+            ref = [sum(e[j] * vals[j][c] for j in range(L)) / tot for c in range(D)]
+            assert np.abs(out[0, h] - np.array(ref)).max() < 1e-6 * np.abs(ref).max() + 1e-7, (kv, h)
+
+
+def test_layout_batched_unpack_equals_per_block():
+    """The batched page unpack used by the full-size comparisons returns what the per-block
+    unpack (pinned above by hand-derived positions and the round trip) returns, page by page."""
+    rng = np.random.default_rng(21)
+    blocks = []
+    for n in (64, 64, 17, 1):
+        kc = rng.integers(0, 4, (n, D), dtype=np.uint8)
+        vc = rng.integers(0, 4, (n, D), dtype=np.uint8)
+        meta = [rng.standard_normal((n, 2)).astype(np.float16) for _ in range(4)]
+        blocks.append(layout.pack_head_block(kc, vc, *meta))
+    batched = layout.unpack_pages(np.stack(blocks))
+    for i, blk in enumerate(blocks):
+        for a, b in zip(batched, layout.unpack_head_block(blk)):
+            assert np.array_equal(np.ascontiguousarray(a[i]).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
