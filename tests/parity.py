@@ -56,44 +56,94 @@ def fp16_ulp_diff(a, b):
     return np.abs(key(a) - key(b))
 
 
+def rotation_error_bound(k_bits, rot_h):
+    """Per-element bound on |x_gpu - k.R| for keys rotated on the matrix cores (bf16 [n, 128] keys,
+    one head's fp32 R): R is carried as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0), each
+    rounding within 2^-8 of its input, so |R - r0 - r1| <= 2^-16 |R|; the products are exact in
+    fp32 and the 8 partial sums (4 K-steps x 2 terms) are each rounded once into the fp32
+    accumulator (2^-24 of at most sum_i |k_i R_ij| each, allowance 2^-20).  Returns [n, 128]."""
+    k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
+    r = np.asarray(rot_h, np.float32).astype(np.float64)
+    return (np.abs(k) @ np.abs(r)) * (2.0 ** -16 + 2.0 ** -20)
+
+
+def _ulp32(x):
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    return np.ldexp(1.0, e - 24)
+
+
+def meta_flip_explained(x_ref, c, s16_gpu, lo16_gpu, elem_bound):
+    """Which fp16 scale / minimum flips of rotated-key groups are explained by the rotation error.
+
+    x_ref: fp64 [n, 128] the oracle's quantizer input; elem_bound: [n, 128] bound on the GPU's
+    input error (rotation_error_bound plus the oracle's own fp32 rounding).  With delta = the
+    group's largest element bound, the group minimum and maximum move by at most delta, so the
+    fp32 scale c (mx - mn) / 3 moves by at most (2c/3) delta and the fp32 minimum
+    mn + (1 - c)(mx - mn)/2 by at most (2 - c) delta, each plus the fp32 roundings of the
+    parameter sequence (a few ulps).  A flip is explained when the oracle's fp32 parameter lies
+    within that distance of the rounding midpoint between the two fp16 values.  Returns boolean
+    arrays (s_ok, lo_ok) [n, 2] (True also where nothing flipped)."""
+    s32, lo32, s16o, lo16o = quantizer.params(np.asarray(x_ref, np.float32), c)
+    delta = np.asarray(elem_bound, np.float64).reshape(len(x_ref), 2, 64).max(axis=-1)
+    xg = np.asarray(x_ref, np.float64).reshape(len(x_ref), 2, 64)
+    span = np.abs(xg).max(axis=-1) + (xg.max(axis=-1) - xg.min(axis=-1))
+    cf = float(c)
+    tol_s = (2 * cf / 3) * delta + 4 * _ulp32(s32)
+    tol_lo = (2 - cf) * delta + 4 * _ulp32(span)
+    mid_s = 0.5 * (s16o.astype(np.float64) + np.asarray(s16_gpu, np.float16).astype(np.float64))
+    mid_lo = 0.5 * (lo16o.astype(np.float64) + np.asarray(lo16_gpu, np.float16).astype(np.float64))
+    s_flip = s16o.view(np.uint16) != np.asarray(s16_gpu, np.float16).view(np.uint16)
+    lo_flip = lo16o.view(np.uint16) != np.asarray(lo16_gpu, np.float16).view(np.uint16)
+    s_ok = ~s_flip | (np.abs(s32.astype(np.float64) - mid_s) <= tol_s)
+    lo_ok = ~lo_flip | (np.abs(lo32.astype(np.float64) - mid_lo) <= tol_lo)
+    return s_ok, lo_ok
+
+
 def compare_int2_unit(gpu_pool, gpu_table, ora_pool, ora_table, seq, gkv, okv, n_int2, x_ref_k, x_ref_v,
-                      check_tail=True):
+                      check_tail=True, k_bound=None):
     """Compare the INT2 tokens of one (seq, kv head) under the parity rules.
 
     x_ref_k / x_ref_v: fp64 [n_int2, 128] values the oracle quantized (rotated keys, values).
+    k_bound: [n_int2, 128] bound on the GPU's key-input error (see rotation_error_bound); when
+    given, every key-metadata flip must be explained by it (``k_meta_unexplained``).
     Returns a dict of counts; asserts nothing (callers assert).
     """
     rep = dict(elements=0, code_mismatch=0, unexplained=0, k_meta_flips=0, v_meta_flips=0,
-               meta_far=0, groups=0, tail_nonzero=0)
+               meta_far=0, groups=0, tail_nonzero=0, k_meta_unexplained=0)
     n_pages = -(-n_int2 // 64)
-    for pg in range(n_pages):
-        n_tok = min(64, n_int2 - 64 * pg)
-        gblk = gpu_pool[gpu_table[seq, pg], gkv]
-        oblk = ora_pool[ora_table[seq, pg], okv]
-        g = layout.unpack_head_block(gblk)
-        o = layout.unpack_head_block(oblk)
-        sl = slice(64 * pg, 64 * pg + n_tok)
-        # unused slots of the last page are zero
-        if check_tail:
-            rep["tail_nonzero"] += int(sum(np.count_nonzero(a[n_tok:]) for a in g))
-        for which, (gc, gs, gl), (oc, os_, ol), xr in (
-                ("k", (g[0], g[2], g[3]), (o[0], o[2], o[3]), x_ref_k[sl]),
-                ("v", (g[1], g[4], g[5]), (o[1], o[4], o[5]), x_ref_v[sl])):
-            gc, oc = gc[:n_tok], oc[:n_tok]
-            gs, gl, os_, ol = gs[:n_tok], gl[:n_tok], os_[:n_tok], ol[:n_tok]
-            flips = (fp16_ulp_diff(gs, os_) > 0) | (fp16_ulp_diff(gl, ol) > 0)
-            far = (fp16_ulp_diff(gs, os_) > 1) | (fp16_ulp_diff(gl, ol) > 1)
-            rep[which + "_meta_flips"] += int(flips.sum())
-            rep["meta_far"] += int(far.sum())
-            rep["groups"] += flips.size
-            mism = gc != oc
-            rep["elements"] += gc.size
-            rep["code_mismatch"] += int(mism.sum())
-            if mism.any():
-                d_o = quantizer.boundary_distance(xr, os_, ol)
-                d_g = quantizer.boundary_distance(xr, gs, gl)
-                explained = (d_o < 1e-3) | (d_g < 1e-3)
-                rep["unexplained"] += int((mism & ~explained).sum())
+    if n_pages == 0:
+        return rep
+    n_last = n_int2 - 64 * (n_pages - 1)
+    g = layout.unpack_pages(gpu_pool[gpu_table[seq, :n_pages], gkv])
+    o = layout.unpack_pages(ora_pool[ora_table[seq, :n_pages], okv])
+    # unused slots of the last page are zero
+    if check_tail and n_last < 64:
+        rep["tail_nonzero"] += int(sum(np.count_nonzero(np.ascontiguousarray(a[-1, n_last:]).view(np.uint8)) for a in g))
+    # flatten pages to token rows, keeping the first n_int2
+    g = [a.reshape((-1,) + a.shape[2:])[:n_int2] for a in g]
+    o = [a.reshape((-1,) + a.shape[2:])[:n_int2] for a in o]
+    for which, (gc, gs, gl), (oc, os_, ol), xr in (
+            ("k", (g[0], g[2], g[3]), (o[0], o[2], o[3]), x_ref_k[:n_int2]),
+            ("v", (g[1], g[4], g[5]), (o[1], o[4], o[5]), x_ref_v[:n_int2])):
+        flips = (fp16_ulp_diff(gs, os_) > 0) | (fp16_ulp_diff(gl, ol) > 0)
+        far = (fp16_ulp_diff(gs, os_) > 1) | (fp16_ulp_diff(gl, ol) > 1)
+        rep[which + "_meta_flips"] += int(flips.sum())
+        if which == "k" and k_bound is not None and flips.any():
+            rows = np.nonzero(flips.any(axis=1))[0]
+            eb = k_bound[rows] + 2.0 ** -24 * np.abs(xr[rows])
+            s_ok, lo_ok = meta_flip_explained(xr[rows], quantizer.C_K, gs[rows], gl[rows], eb)
+            rep["k_meta_unexplained"] += int((~(s_ok & lo_ok)).sum())
+        rep["meta_far"] += int(far.sum())
+        rep["groups"] += flips.size
+        mism = gc != oc
+        rep["elements"] += gc.size
+        rep["code_mismatch"] += int(mism.sum())
+        if mism.any():
+            rows = np.nonzero(mism.any(axis=1))[0]
+            d_o = quantizer.boundary_distance(xr[rows], os_[rows], ol[rows])
+            d_g = quantizer.boundary_distance(xr[rows], gs[rows], gl[rows])
+            explained = (d_o < 1e-3) | (d_g < 1e-3)
+            rep["unexplained"] += int((mism[rows] & ~explained).sum())
     return rep
 
 
@@ -119,3 +169,60 @@ def quant_input_k(k_bits, rot):
 
 def oracle_store_for(hkv, max_seqs, max_pages, num_pages, free, rot):
     return ostore.OracleStore(hkv, max_seqs, max_pages, num_pages, free, rot)
+
+
+def check_evicted(pool, table, ring_before, seq, n2, heads=None):
+    """INT2 index n2 of one sequence against the oracle's quantization of the GPU's ring slot
+    (identical inputs): page-table entry present, metadata bit-exact, codes equal except where
+    the value lies within 1e-3 * s16 of a rounding boundary (the oracle decides in fp64, the
+    kernel in fp32).  Returns the number of explained code mismatches; asserts the rest."""
+    kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(ring_before, seq, n2)
+    slot = ostore.OracleStore.ring_slot(64 + int(n2))
+    page = int(table[seq, n2 // 64])
+    assert page >= 0, (seq, n2)
+    j = n2 % 64
+    explained = 0
+    heads = range(kc.shape[0]) if heads is None else heads
+    for h in heads:
+        g = layout.unpack_head_block(pool[page, h])
+        for isv, (codes, s16, lo16, gc, gs, gl) in enumerate(((kc[h], ksc[h], klo[h], g[0][j], g[2][j], g[3][j]),
+                                                              (vc[h], vsc[h], vlo[h], g[1][j], g[4][j], g[5][j]))):
+            assert np.array_equal(gs.view(np.uint16), s16.view(np.uint16)), (seq, n2, h, isv)
+            assert np.array_equal(gl.view(np.uint16), lo16.view(np.uint16)), (seq, n2, h, isv)
+            mism = gc != codes
+            if mism.any():
+                x = ostore.bf16_to_f64(ring_before[seq, h, isv, slot])
+                d = quantizer.boundary_distance(x[None], s16[None], lo16[None])[0]
+                assert np.all(d[mism] < 1e-3), (seq, n2, h, isv)
+                explained += int(mism.sum())
+    return explained
+
+
+def ring_key_bound(k_bits, rot_h):
+    """Allowed |stored bf16 key - exact k.R| per channel, besides half a bf16 ulp of the stored value.
+    Multi-token writes rotate on the matrix cores with R split into bf16 terms r0 + r1 (each the
+    bf16 rounding of the remainder, within 2^-8 of it, so |R - r0 - r1| <= 2^-16 |R|) and fp32
+    accumulation of the 256 products k_i r0_ij, k_i r1_ij; single-token appends use a 128-term fp32
+    dot product.  Both stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-16 sum_i |k_i R_ij|
+    (dot-product forward-error bound, Higham, Accuracy and Stability of Numerical Algorithms,
+    section 3.1).  Returns (bound, exact k.R) [n, 128]."""
+    k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
+    r = np.asarray(rot_h, np.float32).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = 256 * u / (1 - 256 * u)
+    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -16), k @ r
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    return np.ldexp(1.0, e - 8)
+
+
+def check_ring_keys(got_bits, k_bits, rot_h):
+    """Stored bf16 ring keys [n, 128] of one head within half a bf16 ulp plus ring_key_bound of
+    the exact k.R (asserts)."""
+    bound, xk = ring_key_bound(k_bits, rot_h)
+    got = ostore.bf16_to_f64(got_bits)
+    ulp = np.maximum(bf16_ulp(got), bf16_ulp(xk))
+    assert np.all(np.abs(got - xk) <= 0.5 * ulp + bound)

@@ -13,7 +13,7 @@ import pytest
 import parity
 import synth
 from test_gpu_parity import poison
-from oracle import attention, layout, store as ostore
+from oracle import attention, store as ostore
 
 pytestmark = pytest.mark.gpu
 D = 128
@@ -35,27 +35,37 @@ def _iso_decode_unit(gpu, lens, n2s, rot, q, s, kv, g):
                             [s], SCALE, g)[0]
 
 
-def _check_write_unit(gpu, cfg, layer, s, kv, L_pre, rot, table_row, n2):
-    """Prefill INT2 pages + ring of one unit vs the oracle on the CPU twin's inputs."""
-    kb, vb = synth.unit_kv(cfg, layer, s, kv, L_pre)
-    pages = [int(p) for p in table_row[: -(-max(0, L_pre - 320) // 64)]]
-    n_pages = max(1, len(pages))
-    ora = ostore.OracleStore(1, 1, n_pages, max(pages + [0]) + 1, pages, rot[kv:kv + 1])
-    ora.write([0], kb[None, :, None, :], vb[None, :, None, :])
+def _host_bits(t):
+    """bf16 bits of a device tensor drawn by the generator's GPU twin (bit-identical to the CPU twin)."""
+    return t.cpu().numpy().view(np.uint16)
+
+
+def _check_write_unit(gpu, rot, s, kv, kb, vb, n2):
+    """One (seq, KV head) written by a first write of len(kb) tokens, against the oracle on the same
+    inputs: prefill INT2 pages under the tolerance rules (key-metadata flips explained by the
+    rotation error), sink ring slots and the window slots still holding prefill tokens (values
+    bit-exact, keys within the rotation bound).  kb, vb: bf16 bits [L, 128]."""
+    L_pre = len(kb)
     n_pre = max(0, L_pre - 320)
+    gpool, gring, gtable = gpu
+    pages = [int(p) for p in gtable[s, : -(-n_pre // 64)]]
+    ora = ostore.OracleStore(1, 1, max(1, len(pages)), max(pages + [0]) + 1, pages, rot[kv:kv + 1])
+    ora.write([0], kb[None, :, None, :], vb[None, :, None, :])
     xk = parity.quant_input_k(kb[64:64 + n_pre], rot[kv])
     xv = synth.bf16_bits_to_f32(vb[64:64 + n_pre]).astype(np.float64)
-    gpool, gring, gtable = gpu
-    gt = gtable[s:s + 1]
-    rep = parity.compare_int2_unit(gpool, gt, ora.pool, ora.page_table, 0, kv, 0, n_pre, xk, xv,
-                                   check_tail=(n_pre == n2))
+    rep = parity.compare_int2_unit(gpool, gtable[s:s + 1], ora.pool, ora.page_table, 0, kv, 0, n_pre, xk, xv,
+                                   check_tail=(n_pre == n2),
+                                   k_bound=parity.rotation_error_bound(kb[64:64 + n_pre], rot[kv]))
     assert rep["unexplained"] == 0, rep
     assert rep["code_mismatch"] <= max(1, 1e-4 * rep["elements"]), rep
     assert rep["v_meta_flips"] == 0 and rep["meta_far"] == 0, rep
     assert rep["k_meta_flips"] <= 1e-2 * rep["groups"], rep
-    # sink ring slots: values bit-exact
-    assert np.array_equal(gring[s, kv, 1, :64], vb[:64])
-    print(f"[parity] unit seq={s} kv={kv}: {rep}", flush=True)
+    assert rep["k_meta_unexplained"] == 0, rep
+    positions = np.array(list(range(min(64, L_pre))) + list(range(64 + n2, L_pre)), dtype=np.int64)
+    slots = np.array([ostore.OracleStore.ring_slot(int(p)) for p in positions])
+    assert np.array_equal(gring[s, kv, 1, slots], vb[positions])
+    parity.check_ring_keys(gring[s, kv, 0, slots], kb[positions], rot[kv])
+    print(f"[parity] unit seq={s} kv={kv}: {rep}; ring slots checked {len(slots)}", flush=True)
     return rep
 
 
@@ -67,6 +77,18 @@ def _oracle_table(n_seqs_lengths, max_pages, num_pages, free):
         for i in range(-(-n_int2 // 64)):
             st.page_table[s, i] = st.free.popleft()
     return st.page_table
+
+
+def _decode_units(out, gpu, lens, n2s, rot, q, units, g):
+    """Decode outputs of the listed (seq, kv) units against the oracle on the GPU's exported state."""
+    worst = 0.0
+    for s, kv in units:
+        iso = _iso_decode_unit(gpu, lens, n2s, rot, q, s, kv, g)
+        err = parity.rel_l2(out[s, kv * g:(kv + 1) * g], iso)
+        print(f"[parity] decode unit seq={s} kv={kv} rel-l2 {err:.2e}", flush=True)
+        assert err <= 1e-3, (s, kv, err)
+        worst = max(worst, err)
+    return worst
 
 
 def test_qwen3_4b_full_context(gpu_lib):
@@ -99,31 +121,24 @@ def test_qwen3_4b_full_context(gpu_lib):
     for s in seqs:   # eviction of INT2 index L-320 starts page 507 of each sequence, in call order
         ora_t.page_table[s, (L - 320) // 64] = ora_t.free.popleft()
     assert np.array_equal(gpu[2], ora_t.page_table)
-    for s, kv in [(0, 0), (5, 6)]:
-        _check_write_unit(gpu, cfg, 0, s, kv, L, rot, gpu[2][s], L - 320 + 1)
-        # evicted token (INT2 index L-320) vs the oracle on the GPU's ring before eviction
-        kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(before[1], s, L - 320)
-        blk = layout.unpack_head_block(gpu[0][gpu[2][s, (L - 320) // 64], kv])
-        j = (L - 320) % 64
-        assert np.array_equal(blk[0][j], kc[kv]) and np.array_equal(blk[1][j], vc[kv])
-        assert np.array_equal(blk[2][j], ksc[kv]) and np.array_equal(blk[5][j], vlo[kv])
+    for s, kv in [(0, 0), (5, 6), (2, 3), (7, 7)]:
+        _check_write_unit(gpu, rot, s, kv, _host_bits(kbuf[s, :L, kv]), _host_bits(vbuf[s, :L, kv]), L - 320 + 1)
+    explained = 0
+    for s in seqs:   # the evicted token (INT2 index L-320) of every (seq, head), on the GPU's ring
+        explained += parity.check_evicted(gpu[0], gpu[2], before[1], s, L - 320)
+    print(f"[parity] evictions: {B * hkv} token-heads, explained code mismatches {explained}", flush=True)
     q = synth.decode_queries(cfg, 0, B, hq, hkv)
     out = st.decode(seqs, parity.to_dev_bf16(q), SCALE).cpu().numpy()
-    lens = np.full(B, L + 1)
-    n2s = np.full(B, L - 320 + 1)
-    g = hq // hkv
-    for s, kv in [(0, 0), (5, 6), (7, 3)]:
-        iso = _iso_decode_unit(gpu, lens, n2s, rot, q, s, kv, g)
-        err = parity.rel_l2(out[s, kv * g:(kv + 1) * g], iso)
-        print(f"[parity] decode unit seq={s} kv={kv} rel-l2 {err:.2e}", flush=True)
-        assert err <= 1e-3
+    units = [(0, 0), (5, 6), (7, 3), (1, 1), (2, 7), (3, 2), (4, 5), (6, 4)]
+    _decode_units(out, gpu, np.full(B, L + 1), np.full(B, L - 320 + 1), rot, q, units, hq // hkv)
 
 
 def test_qwen3_8b_layer_100k_b32(gpu_lib):
     """One layer of the 36-layer Qwen3-8B-shaped step at full size (32 q / 8 kv heads, batch 32,
     100000-token context, shuffled physical pages), in the launch configuration the benchmark
     times: one-call decode steps (write + attention).  Page table exact; sampled units' INT2
-    pages, evicted tokens and decode outputs against the oracle."""
+    pages and ring, every (seq, head)'s evicted tokens, and 8 units' decode outputs against the
+    oracle."""
     import torch
     from synth import gpu as sg
     cfg, hkv, hq, B, L = synth.CFG_QWEN3_8B, 8, 32, 32, 100000
@@ -140,11 +155,16 @@ def test_qwen3_8b_layer_100k_b32(gpu_lib):
     vbuf = torch.empty_like(kbuf)
     newk = torch.empty((2, B, hkv, D), dtype=torch.int16, device="cuda")
     newv = torch.empty_like(newk)
+    write_units = [(0, 0), (19, 5), (31, 2), (8, 7)]
+    inputs = {}
     for s in range(B):
         sg.draw_kv(prm, s, 0, L + 2, kbuf[0], vbuf[0])
         st.write([s], kbuf[:, :L], vbuf[:, :L])
         newk[:, s] = kbuf[0, L:L + 2]
         newv[:, s] = vbuf[0, L:L + 2]
+        for s2, kv in write_units:
+            if s2 == s:
+                inputs[(s, kv)] = (_host_bits(kbuf[0, :L, kv]), _host_bits(vbuf[0, :L, kv]))
     del kbuf, vbuf
     seqs = list(range(B))
     q = synth.decode_queries(cfg, 0, B, hq, hkv)
@@ -158,30 +178,21 @@ def test_qwen3_8b_layer_100k_b32(gpu_lib):
     # no page: (L-320) % 64 = 32)
     ora_t = _oracle_table([L] * B, max_pages, num_pages, free)
     assert np.array_equal(after[2], ora_t)
-    for s, kv in [(0, 0), (19, 5)]:
-        _check_write_unit(gpu, cfg, 0, s, kv, L, rot, gpu[2][s], L - 320 + 1)
-        kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(before[1], s, L - 320)
-        blk = layout.unpack_head_block(gpu[0][gpu[2][s, (L - 320) // 64], kv])
-        j = (L - 320) % 64
-        assert np.array_equal(blk[0][j], kc[kv]) and np.array_equal(blk[1][j], vc[kv])
-        assert np.array_equal(blk[2][j], ksc[kv]) and np.array_equal(blk[3][j], klo[kv])
-        assert np.array_equal(blk[4][j], vsc[kv]) and np.array_equal(blk[5][j], vlo[kv])
-    lens = np.full(B, L + 2)
-    n2s = np.full(B, L - 320 + 2)
-    g = hq // hkv
-    for s, kv in [(0, 0), (19, 5), (31, 7)]:
-        iso = _iso_decode_unit(after, lens, n2s, rot, q, s, kv, g)
-        err = parity.rel_l2(out[s, kv * g:(kv + 1) * g], iso)
-        print(f"[parity] decode unit seq={s} kv={kv} rel-l2 {err:.2e}", flush=True)
-        assert err <= 1e-3
+    for (s, kv), (kb, vb) in inputs.items():
+        _check_write_unit(gpu, rot, s, kv, kb, vb, L - 320 + 1)
+    explained = 0
+    for s in seqs:
+        explained += parity.check_evicted(gpu[0], gpu[2], before[1], s, L - 320)
+        explained += parity.check_evicted(after[0], after[2], gpu[1], s, L - 320 + 1)
+    print(f"[parity] evictions: {2 * B * hkv} token-heads, explained code mismatches {explained}", flush=True)
+    units = [(0, 0), (19, 5), (31, 7), (4, 1), (8, 2), (12, 3), (25, 4), (28, 6)]
+    _decode_units(out, after, np.full(B, L + 2), np.full(B, L - 320 + 2), rot, q, units, hq // hkv)
 
 
-def test_prefill_131072_then_1024_appends(gpu_lib):
-    """One 131072-token sequence x 8 KV heads, then 1024 decode-step writes (evict 1 + append 1 each)."""
+def _prefill_131072(gpu_lib, n_app):
     import torch
     from synth import gpu as sg
-    cfg, hkv, hq, L, n_app = synth.CFG_PREFILL, 8, 32, 131072, 1024
-    _case("prefill 131072 + 1024 appends")
+    cfg, hkv, hq, L = synth.CFG_PREFILL, 8, 32, 131072
     rot = parity.calibrate(cfg, 0, hkv)
     max_pages = -(-(L + n_app) // 64) + 1
     st = gpu_lib.KVStore(hq, hkv, 1, max_pages, max_pages)
@@ -192,35 +203,62 @@ def test_prefill_131072_then_1024_appends(gpu_lib):
     vbuf = torch.empty_like(kbuf)
     sg.draw_kv(prm, 0, 0, L + n_app, kbuf[0], vbuf[0])
     st.write([0], kbuf[:, :L].contiguous(), vbuf[:, :L].contiguous())
+    return cfg, hkv, hq, L, rot, st, kbuf, vbuf
+
+
+def test_prefill_131072_all_heads(gpu_lib):
+    """One 131072-token sequence x 8 KV heads written in one call: page table, the BF16 share, and
+    every head's INT2 pages and ring slots against the oracle."""
+    _case("prefill 131072, all 8 heads")
+    cfg, hkv, hq, L, rot, st, kbuf, vbuf = _prefill_131072(gpu_lib, 0)
     gpu = parity.export(st)
     ln, n2 = st.seq_info(0)
     assert (ln, n2) == (131072, 131072 - 320)
     assert round(100 * (ln - n2) / ln, 2) == 0.24          # the pages' 0.24 % BF16 share at 128K
-    assert np.array_equal(gpu[2][0, :2043], np.arange(2043)) and gpu[2][0, 2043] == -1
-    for kv in (0, 7):
-        _check_write_unit(gpu, cfg, 0, 0, kv, L, rot, gpu[2][0], n2)
-    ring_before = None
+    assert np.array_equal(gpu[2][0, :2043], np.arange(2043)) and (gpu[2][0, 2043:] == -1).all()
+    tot = dict(elements=0, code_mismatch=0, k_meta_flips=0, groups=0)
+    for kv in range(hkv):
+        rep = _check_write_unit(gpu, rot, 0, kv, _host_bits(kbuf[0, :, kv]), _host_bits(vbuf[0, :, kv]), n2)
+        for k in tot:
+            tot[k] += rep[k]
+    print(f"[parity] all heads: {tot}", flush=True)
+
+
+def test_prefill_131072_then_1024_appends(gpu_lib):
+    """One 131072-token sequence x 8 KV heads, then 1024 decode-step writes (evict 1 + append 1
+    each): every 64th eviction checked for all heads on the GPU's own ring, the appended tokens'
+    ring keys and values after the last step, the page table, and decode on the final state."""
+    import torch
+    n_app = 1024
+    _case("prefill 131072 + 1024 appends")
+    cfg, hkv, hq, L, rot, st, kbuf, vbuf = _prefill_131072(gpu_lib, n_app)
+    explained = checked = 0
     for i in range(n_app):
-        if i == n_app - 1:
-            ring_before = parity.export(st)[1]
+        ring_before = None
+        if i % 64 == 0 or i == n_app - 1:
+            torch.cuda.synchronize()
+            ring_before = st.ring_view().cpu().numpy().view(np.uint16)
         st.decode_write([0], kbuf[:, L + i].contiguous(), vbuf[:, L + i].contiguous())
+        if ring_before is not None:
+            after = parity.export(st)
+            explained += parity.check_evicted(after[0], after[2], ring_before, 0, L - 320 + i)
+            checked += 1
     gpu = parity.export(st)
     assert st.seq_info(0) == (L + n_app, L + n_app - 320)
+    print(f"[parity] evictions checked {checked} x {hkv} heads, explained code mismatches {explained}", flush=True)
     n_pages_now = -(-(L + n_app - 320) // 64)
     assert np.array_equal(gpu[2][0, :n_pages_now], np.arange(n_pages_now)) and (gpu[2][0, n_pages_now:] == -1).all()
-    idx = L + n_app - 320 - 1
-    kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(ring_before, 0, idx)
+    # the window now holds appended tokens only (single-token rotation on the VALU)
+    positions = np.arange(L + n_app - 256, L + n_app)
+    slots = np.array([ostore.OracleStore.ring_slot(int(p)) for p in positions])
     for kv in range(hkv):
-        blk = layout.unpack_head_block(gpu[0][gpu[2][0, idx // 64], kv])
-        j = idx % 64
-        assert np.array_equal(blk[0][j], kc[kv]) and np.array_equal(blk[1][j], vc[kv])
-        assert np.array_equal(blk[2][j], ksc[kv]) and np.array_equal(blk[3][j], klo[kv])
+        kb = _host_bits(kbuf[0, L + n_app - 256:L + n_app, kv])
+        assert np.array_equal(gpu[1][0, kv, 1, slots], _host_bits(vbuf[0, L + n_app - 256:L + n_app, kv]))
+        parity.check_ring_keys(gpu[1][0, kv, 0, slots], kb, rot[kv])
     q = synth.decode_queries(cfg, 0, 1, hq, hkv)
     out = st.decode([0], parity.to_dev_bf16(q), SCALE).cpu().numpy()
-    g = hq // hkv
-    for kv in (0, 5):
-        iso = _iso_decode_unit(gpu, np.array([L + n_app]), np.array([L + n_app - 320]), rot, q, 0, kv, g)
-        assert parity.rel_l2(out[0, kv * g:(kv + 1) * g], iso) <= 1e-3
+    _decode_units(out, gpu, np.array([L + n_app]), np.array([L + n_app - 320]), rot, q, [(0, 0), (0, 5)],
+                  hq // hkv)
 
 
 def test_qwen3_32b_ragged_full(gpu_lib):
@@ -240,23 +278,22 @@ def test_qwen3_32b_ragged_full(gpu_lib):
     prm = sg.HeadParams(cfg, 0, hkv)
     kbuf = torch.empty((1, max(lengths), hkv, D), dtype=torch.int16, device="cuda")
     vbuf = torch.empty_like(kbuf)
+    s_short, s_long = int(np.argmin(lengths)), int(np.argmax(lengths))
+    inputs = {}
     for s, L in enumerate(lengths):
         sg.draw_kv(prm, s, 0, L, kbuf[0, :L], vbuf[0, :L])
         st.write([s], kbuf[:, :L], vbuf[:, :L])
+        for s2, kv in ((s_short, 3), (s_long, 6)):
+            if s2 == s:
+                inputs[(s, kv)] = (_host_bits(kbuf[0, :L, kv]), _host_bits(vbuf[0, :L, kv]))
     del kbuf, vbuf
     gpu = parity.export(st)
     assert np.array_equal(gpu[2], _oracle_table(lengths, max_pages, num_pages, free))
-    s_short = int(np.argmin(lengths))
-    _check_write_unit(gpu, cfg, 0, s_short, 3, lengths[s_short], rot, gpu[2][s_short], lengths[s_short] - 320)
+    for (s, kv), (kb, vb) in inputs.items():
+        _check_write_unit(gpu, rot, s, kv, kb, vb, lengths[s] - 320)
     seqs = list(range(B))
     q = synth.decode_queries(cfg, 0, B, hq, hkv)
     out = st.decode(seqs, parity.to_dev_bf16(q), SCALE).cpu().numpy()
     lens = np.array(lengths)
-    n2s = lens - 320
-    g = hq // hkv
-    s_long = int(np.argmax(lengths))
-    for s, kv in [(s_short, 0), (s_long, 7), (3, 4)]:
-        iso = _iso_decode_unit(gpu, lens, n2s, rot, q, s, kv, g)
-        err = parity.rel_l2(out[s, kv * g:(kv + 1) * g], iso)
-        print(f"[parity] decode unit seq={s} (L={lengths[s]}) kv={kv} rel-l2 {err:.2e}", flush=True)
-        assert err <= 1e-3
+    units = [(s_short, 0), (s_long, 7), (3, 4), (0, 1), (5, 2), (9, 3), (12, 5), (15, 6)]
+    _decode_units(out, gpu, lens, lens - 320, rot, q, units, hq // hkv)

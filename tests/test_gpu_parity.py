@@ -16,12 +16,21 @@ D = 128
 SCALE = 1.0 / math.sqrt(D)
 # Decode parity is checked on identical cache state (oracle run on the GPU's exported store):
 # rel-L2 <= 1e-3.  End to end (each side on its own store) the outputs also differ by the write
-# path's allowed rounding: fp32 rotation vs the oracle's fp64 product flips a few codes that lie
-# within 1e-3 * scale of a rounding boundary, each moving one key element by a full quantization
-# step.  A CPU emulation of an fp32 rotation reproduces the measured end-to-end deviation exactly
-# (1.6e-3 on the ragged GQA-8 case), so the end-to-end bound is looser.
+# path's allowed rounding: the fp32 rotation on the matrix cores vs the oracle's fp64 product
+# flips a few codes that lie within 1e-3 * scale of a rounding boundary (and a few key scales /
+# minimums by one fp16 ulp), each moving one key element by a full quantization step.  A CPU
+# emulation of the fp32 rotation reproduces the largest measured end-to-end deviation (1.6e-3, a
+# ragged GQA-8 sequence); the bound below is twice that, and every test prints its maximum.
 ISO_TOL = 1e-3
-E2E_TOL = 1e-2
+E2E_TOL = 3e-3
+
+
+def _e2e(out, ref, what=""):
+    """End-to-end rel-L2 (each side on its own store) within E2E_TOL; prints the value."""
+    err = parity.rel_l2(out, ref)
+    print(f"[e2e] {what} rel-l2 {err:.2e}", flush=True)
+    assert err <= E2E_TOL, (what, err)
+    return err
 
 
 def _case(name):
@@ -52,26 +61,6 @@ def _kv_batch(cfg, seqs, hkv, n, token0=0):
     return ks, vs
 
 
-def _ring_key_bound(k_bits, rot_h):
-    """Allowed |stored bf16 key - exact k.R| per channel, besides half a bf16 ulp of the stored value.
-    Multi-token writes rotate on the matrix cores with R split into bf16 terms r0 + r1 (each the
-    bf16 rounding of the remainder, so |R - r0 - r1| <= 2^-18 |R|) and fp32 accumulation of the
-    256 products k_i r0_ij, k_i r1_ij; single-token appends use a 128-term fp32 dot product.  Both
-    stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-18 sum_i |k_i R_ij| (dot-product
-    forward-error bound, Higham, Accuracy and Stability of Numerical Algorithms, section 3.1)."""
-    k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
-    r = np.asarray(rot_h, np.float32).astype(np.float64)
-    u = 2.0 ** -24
-    gamma = 256 * u / (1 - 256 * u)
-    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -18), k @ r
-
-
-def _bf16_ulp(x):
-    """Spacing of bf16 numbers at |x| (8 significant bits)."""
-    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
-    return np.ldexp(1.0, e - 8)
-
-
 def _check_state(gpu, ora, seqs, rot, inputs):
     """Page tables exact; ring V bit-exact, ring K within the fp32 rotation error bound; INT2 pages
     written by the first (prefill) write under the tolerance rules.
@@ -81,7 +70,7 @@ def _check_state(gpu, ora, seqs, rot, inputs):
     gpool, gring, gtable = gpu
     assert np.array_equal(gtable, ora.page_table)
     totals = dict(elements=0, code_mismatch=0, unexplained=0, k_meta_flips=0, v_meta_flips=0, meta_far=0,
-                  groups=0, tail_nonzero=0)
+                  groups=0, tail_nonzero=0, k_meta_unexplained=0)
     k_ulp_flips = 0
     for s in seqs:
         L, n2 = int(ora.length[s]), int(ora.n_int2[s])
@@ -91,10 +80,7 @@ def _check_state(gpu, ora, seqs, rot, inputs):
             slots = np.array([ora.ring_slot(int(p)) for p in positions])
             assert np.array_equal(gring[s, :, 1, slots], ora.ring[s, :, 1, slots]), s
             for h in range(ora.hkv):
-                bound, xk = _ring_key_bound(kb[positions, h], rot[h])
-                got = ostore.bf16_to_f64(gring[s, h, 0, slots])
-                ulp = np.maximum(_bf16_ulp(got), _bf16_ulp(xk))
-                assert np.all(np.abs(got - xk) <= 0.5 * ulp + bound), (s, h)
+                parity.check_ring_keys(gring[s, h, 0, slots], kb[positions, h], rot[h])
                 k_ulp_flips += int((gring[s, h, 0, slots] != ora.ring[s, h, 0, slots]).sum())
         # prefill INT2 tokens only: evicted ones are checked bit-exactly by the callers against the
         # oracle run on the GPU's own ring (identical inputs)
@@ -105,30 +91,24 @@ def _check_state(gpu, ora, seqs, rot, inputs):
             xk = parity.quant_input_k(kb[64:64 + n_pre, h], rot[h])
             xv = synth.bf16_bits_to_f32(vb[64:64 + n_pre, h]).astype(np.float64)
             rep = parity.compare_int2_unit(gpool, gtable, ora.pool, ora.page_table, s, h, h, n_pre, xk, xv,
-                                           check_tail=(n_pre == n2))
+                                           check_tail=(n_pre == n2),
+                                           k_bound=parity.rotation_error_bound(kb[64:64 + n_pre, h], rot[h]))
             for k in totals:
                 totals[k] += rep[k]
     assert totals["unexplained"] == 0, totals
     assert totals["code_mismatch"] <= max(1, 1e-4 * totals["elements"]), totals
     assert totals["v_meta_flips"] == 0 and totals["meta_far"] == 0, totals
     assert totals["k_meta_flips"] <= 1e-2 * max(1, totals["groups"]), totals
+    assert totals["k_meta_unexplained"] == 0, totals
     assert totals["tail_nonzero"] == 0, totals
     print(f"[parity] {totals} ring-key bf16 differences: {k_ulp_flips}", flush=True)
     return totals, k_ulp_flips
 
 
 def _check_evicted(after, ring_before, seqs, hkv, n2):
-    """INT2 index n2 of every listed sequence equals the oracle's quantization of the GPU's ring slot."""
-    from oracle import layout
-    for s in seqs:
-        page = after[2][s, n2 // 64]
-        kc, ksc, klo, vc, vsc, vlo = ostore.evict_from_ring(ring_before, s, n2)
-        for h in range(hkv):
-            g = layout.unpack_head_block(after[0][page, h])
-            j = n2 % 64
-            assert np.array_equal(g[0][j], kc[h]) and np.array_equal(g[1][j], vc[h]), (s, h)
-            assert np.array_equal(g[2][j], ksc[h]) and np.array_equal(g[3][j], klo[h]), (s, h)
-            assert np.array_equal(g[4][j], vsc[h]) and np.array_equal(g[5][j], vlo[h]), (s, h)
+    """INT2 index n2 of every listed sequence equals the oracle's quantization of the GPU's ring
+    slot: metadata bit-exact, codes exact except within the 1e-3 band (parity.check_evicted)."""
+    return sum(parity.check_evicted(after[0], after[2], ring_before, s, n2) for s in seqs)
 
 
 def test_generator_gpu_twin_bit_exact(gpu_lib):
@@ -166,7 +146,7 @@ def test_tiny_config_write_and_decode(gpu_lib):
     iso = attention.decode(*gpu[:2], gpu[2], ora.length, ora.n_int2, rot, q, [0], SCALE, hq)
     assert parity.rel_l2(out, iso) <= ISO_TOL
     ref = attention.decode_store(ora, q, [0], SCALE, hq)
-    assert parity.rel_l2(out, ref) <= E2E_TOL
+    _e2e(out, ref)
 
 
 @pytest.mark.parametrize("gqa", [1, 4, 8])
@@ -196,7 +176,7 @@ def test_edge_lengths_ragged_shuffled_pages(gpu_lib, gqa):
     iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
     for b in range(len(seqs)):
         assert parity.rel_l2(out[b], iso[b]) <= ISO_TOL, (b, lengths[b])
-        assert parity.rel_l2(out[b], ref[b]) <= E2E_TOL, (b, lengths[b])
+        _e2e(out[b], ref[b], (b, lengths[b]))
 
 
 def test_evict_append_decode_cycle(gpu_lib):
@@ -229,7 +209,7 @@ def test_evict_append_decode_cycle(gpu_lib):
             iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
             assert parity.rel_l2(out, iso) <= ISO_TOL, step
             ref = attention.decode_store(ora, q, seqs, SCALE, hq)
-            assert parity.rel_l2(out, ref) <= E2E_TOL, step
+            _e2e(out, ref, step)
     for s in seqs:
         assert st.seq_info(s) == (470, 470 - 320)
 
@@ -280,7 +260,7 @@ def test_fused_decode_write_matches_evict_then_write(gpu_lib):
     iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
     assert parity.rel_l2(out, iso) <= ISO_TOL
     ref = attention.decode_store(ora, q, ids, SCALE, hq)
-    assert parity.rel_l2(out, ref) <= E2E_TOL
+    _e2e(out, ref)
 
 
 def _extreme_tokens(rng, n):
@@ -373,7 +353,7 @@ def test_more_sequences_than_one_launch(gpu_lib):
     for b in range(n):
         assert parity.rel_l2(out[b], iso[b]) <= ISO_TOL, b
     ref = attention.decode_store(ora, q, ids[::-1], SCALE, hq)
-    assert parity.rel_l2(out, ref) <= E2E_TOL
+    _e2e(out, ref)
 
 
 @pytest.mark.parametrize("kernel", [0, 1])
@@ -457,7 +437,7 @@ def test_evicting_write_matches_token_by_token(gpu_lib):
     iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
     assert parity.rel_l2(out, iso) <= ISO_TOL
     ref = attention.decode_store(ora, q, seqs, SCALE, hq)
-    assert parity.rel_l2(out, ref) <= E2E_TOL
+    _e2e(out, ref)
 
 
 @pytest.mark.parametrize("kernel", [0, 1])
@@ -512,7 +492,7 @@ def test_decode_step_one_call_matches_two_calls(gpu_lib, kernel):
             iso = attention.decode(a[0], a[1], a[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
             assert parity.rel_l2(out1, iso) <= ISO_TOL, step
             ref = attention.decode_store(ora, q, ids, SCALE, hq)
-            assert parity.rel_l2(out1, ref) <= E2E_TOL, step
+            _e2e(out1, ref, step)
     assert np.array_equal(parity.export(one)[2], ora.page_table)
 
 
@@ -593,7 +573,7 @@ def test_qwen3_4b_shape_small_context(gpu_lib):
     iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
     assert parity.rel_l2(out, iso) <= ISO_TOL
     ref = attention.decode_store(ora, q, seqs, SCALE, hq)
-    assert parity.rel_l2(out, ref) <= E2E_TOL
+    _e2e(out, ref)
 
 
 def test_qwen3_32b_shape_ragged_small(gpu_lib):
@@ -621,6 +601,6 @@ def test_qwen3_32b_shape_ragged_small(gpu_lib):
     iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
     for b in range(B):
         assert parity.rel_l2(out[b], iso[b]) <= ISO_TOL, b
-        assert parity.rel_l2(out[b], ref[b]) <= E2E_TOL, b
+        _e2e(out[b], ref[b], b)
     print(f"[parity] e2e rel-l2 max {max(parity.rel_l2(out[b], ref[b]) for b in range(B)):.2e} "
           f"iso max {max(parity.rel_l2(out[b], iso[b]) for b in range(B)):.2e}", flush=True)

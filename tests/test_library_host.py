@@ -355,3 +355,23 @@ def test_decode_write_errors_leave_state_unchanged():
     with pytest.raises(oscar.OscarError) as e:
         s.decode_write([1], None, None)            # needs a page, none free
     assert e.value.status == oscar.E_NOPAGE
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks every device tensor it hands to the library (shape, dtype, contiguity,
+    device) before the call, so a wrong one raises instead of reading or writing out of bounds."""
+    import torch
+    import decode_attention_write_amd as oscar
+    ok = torch.zeros((2, 3, 4, 128), dtype=torch.int16)
+    oscar.check_tensor(ok, "k", (2, 3, 4, 128), (torch.int16, torch.bfloat16))
+    bad = [
+        (torch.zeros((2, 3, 5, 128), dtype=torch.int16), "shape"),              # wrong Hkv
+        (torch.zeros((2, 3, 4, 128), dtype=torch.float32), "dtype"),            # fp32 where bf16
+        (torch.zeros((2, 3, 4, 256), dtype=torch.int16)[..., ::2], "contiguous"),
+        (torch.zeros((2, 4, 4, 128), dtype=torch.int16)[:, 1:], "contiguous"),  # a slice of a longer buffer
+    ]
+    for t, what in bad:
+        with pytest.raises(ValueError, match=what):
+            oscar.check_tensor(t, "k", (2, 3, 4, 128), (torch.int16, torch.bfloat16))
+    with pytest.raises(ValueError, match="on cpu"):
+        oscar.check_tensor(ok, "k", (2, 3, 4, 128), (torch.int16,), torch.device("meta"))
