@@ -120,6 +120,39 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def check_tensor(t, name, shape, dtypes, device=None):
+    """Raise ValueError unless t is a contiguous tensor of exactly `shape` whose dtype is one of
+    `dtypes` (on `device`, when given).  The library reads and writes raw device memory through
+    these pointers, so a wrong size, stride or element width would go out of bounds silently."""
+    if t is None:
+        raise ValueError(f"{name}: missing tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)   # bf16 values or their raw bits
+
+
+def _out_types(store):
+    import torch
+    return (torch.bfloat16,) if store.out_bf16 else (torch.float32,)
+
+
+def _check_ws(ws, device):
+    if ws is None or not ws.is_contiguous():
+        raise ValueError("ws: missing or not contiguous")
+    if device is not None and ws.device != device:
+        raise ValueError(f"ws: on {ws.device}, expected {device}")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -175,7 +208,11 @@ def oscar_fold_value_rotation(w_v, w_o, r_v, num_q_heads, num_kv_heads):
 def oscar_kv_write(store, seq_ids, k, v, stream=None):
     """k, v: bf16 device tensors [n_seqs, n_new, Hkv, 128] (contiguous)."""
     ids, p = _i32(seq_ids)
-    n_new = int(k.shape[1]) if k is not None else 0
+    if k is None or k.dim() != 4:
+        raise ValueError("k must be [n_seqs, n_new, Hkv, 128]")
+    n_new = int(k.shape[1])
+    for t, name in ((k, "k"), (v, "v")):
+        check_tensor(t, name, (len(ids), n_new, store.hkv, HEAD_DIM), _bf16_types(), store.device)
     _check(load().oscar_kv_write(store.handle, p, len(ids), n_new, _ptr(k), _ptr(v),
                                  None if store.plan_only else _stream(stream)))
 
@@ -190,6 +227,9 @@ def oscar_kv_decode_write(store, seq_ids, k, v, stream=None):
     """The decode step's write: evict when the window is full, then append one token.
     k, v: bf16 device tensors [n_seqs, Hkv, 128] (contiguous)."""
     ids, p = _i32(seq_ids)
+    if not store.plan_only:
+        for t, name in ((k, "k"), (v, "v")):
+            check_tensor(t, name, (len(ids), store.hkv, HEAD_DIM), _bf16_types(), store.device)
     _check(load().oscar_kv_decode_write(store.handle, p, len(ids), _ptr(k), _ptr(v),
                                         None if store.plan_only else _stream(stream)))
 
@@ -202,11 +242,18 @@ def oscar_decode_workspace_bytes(store, seq_ids):
 
 
 def oscar_decode_attn(store, seq_ids, q, sm_scale, out, ws, stream=None):
-    """q: bf16 [n_seqs, Hq, 128]; out: fp32 [n_seqs, Hq, 128]; ws: device workspace tensor."""
+    """q: bf16 [n_seqs, Hq, 128]; out: fp32 [n_seqs, Hq, 128] (bf16 when the store's output is
+    bf16); ws: device workspace tensor."""
     ids, p = _i32(seq_ids)
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    if store.plan_only:
+        _check(load().oscar_decode_attn(store.handle, p, len(ids), None, ctypes.c_float(sm_scale), None, None, 0, None))
+        return
+    check_tensor(q, "q", (len(ids), store.hq, HEAD_DIM), _bf16_types(), store.device)
+    check_tensor(out, "out", (len(ids), store.hq, HEAD_DIM), _out_types(store), store.device)
+    _check_ws(ws, store.device)
+    nbytes = ws.numel() * ws.element_size()
     _check(load().oscar_decode_attn(store.handle, p, len(ids), _ptr(q), ctypes.c_float(sm_scale), _ptr(out),
-                                    _ptr(ws), nbytes, None if store.plan_only else _stream(stream)))
+                                    _ptr(ws), nbytes, _stream(stream)))
 
 
 def oscar_decode_step_workspace_bytes(store, seq_ids):
@@ -220,9 +267,18 @@ def oscar_decode_step(store, seq_ids, k, v, q, sm_scale, out, ws, stream=None):
     """One whole decode step (the decode-step write of k, v, then attention of q over everything
     stored).  k, v: bf16 [n_seqs, Hkv, 128]; q: bf16 [n_seqs, Hq, 128]; out: fp32 [n_seqs, Hq, 128]."""
     ids, p = _i32(seq_ids)
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    if store.plan_only:
+        _check(load().oscar_decode_step(store.handle, p, len(ids), None, None, None, ctypes.c_float(sm_scale),
+                                        None, None, 0, None))
+        return
+    for t, name in ((k, "k"), (v, "v")):
+        check_tensor(t, name, (len(ids), store.hkv, HEAD_DIM), _bf16_types(), store.device)
+    check_tensor(q, "q", (len(ids), store.hq, HEAD_DIM), _bf16_types(), store.device)
+    check_tensor(out, "out", (len(ids), store.hq, HEAD_DIM), _out_types(store), store.device)
+    _check_ws(ws, store.device)
+    nbytes = ws.numel() * ws.element_size()
     _check(load().oscar_decode_step(store.handle, p, len(ids), _ptr(k), _ptr(v), _ptr(q), ctypes.c_float(sm_scale),
-                                    _ptr(out), _ptr(ws), nbytes, None if store.plan_only else _stream(stream)))
+                                    _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------- store object
@@ -237,6 +293,7 @@ class KVStore:
         self.max_seqs, self.max_pages, self.num_pages = max_seqs, max_pages_per_seq, num_pages
         self.plan_only = plan_only
         self.out_bf16 = False
+        self.device = None
         d = _Desc(num_q_heads, num_kv_heads, max_seqs, max_pages_per_seq, num_pages,
                   FLAG_PLAN_ONLY if plan_only else 0, None, None, None, None)
         sizes = [ctypes.c_size_t(0) for _ in range(4)]
@@ -249,6 +306,7 @@ class KVStore:
             self.ring = torch.empty(self.bytes["ring"] // 2, dtype=torch.int16, device=device)
             self.page_table_dev = torch.empty(self.bytes["page_table"] // 4, dtype=torch.int32, device=device)
             self.rot = torch.empty(self.bytes["rot"], dtype=torch.uint8, device=device)
+            self.device = self.pool.device
             d.pool, d.ring = self.pool.data_ptr(), self.ring.data_ptr()
             d.page_table, d.rot = self.page_table_dev.data_ptr(), self.rot.data_ptr()
         fp = np.arange(num_pages, dtype=np.int32) if free_pages is None else np.asarray(free_pages, dtype=np.int32)

@@ -1,8 +1,10 @@
 // Host runtime of liboscar: the store handle, argument validation, the FIFO
 // page allocator with its page-table mirror, split planning and the C ABI.
 //
-// Every call validates completely before it changes anything, so a failing
-// call leaves the store as it was.  All per-call plans travel to the kernels in
+// Every call validates completely before it changes anything, so a call that
+// fails validation leaves the store as it was.  A HIP failure after a call has
+// committed its host bookkeeping marks the handle unusable (its mirror may be
+// ahead of the device), and later calls on it are refused.  All per-call plans travel to the kernels in
 // kernel arguments; the only host-to-device traffic besides that is the
 // rotation upload and page-table updates (small scatter launches).
 #include <hip/hip_runtime.h>
@@ -49,6 +51,9 @@ struct oscar_kv {
   int32_t write_evicts = 0;    // 1: a write that overflows a non-empty window evicts as it goes
   int32_t out_bf16 = 0;        // 1: decode outputs are written as bf16
   bool has_rotation = false;
+  // A HIP failure after a call has committed its host bookkeeping (page table mirror, FIFO,
+  // lengths) leaves the mirror ahead of the device: the handle then refuses every further call.
+  bool broken = false;
   // timing events per timed kernel: 2 * OSCAR_TIMING_PAIRS each when timing is on
   std::vector<hipEvent_t> timing_ev[2];
   mutable int32_t timing_used[2] = {0, 0};  // pairs recorded since the last read (decode takes a const handle)
@@ -74,6 +79,22 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int hip_fail(hipError_t e, const char* what) {
   set_error("%s: %s", what, hipGetErrorString(e));
   return OSCAR_E_HIP;
+}
+
+// A HIP failure of a call that has already moved the host mirror: mark the handle unusable.
+int hip_fail_committed(oscar_kv* kv, hipError_t e, const char* what) {
+  kv->broken = true;
+  return hip_fail(e, what);
+}
+
+// Every call on a handle first checks that no earlier call left it unusable.
+int check_usable(const oscar_kv* kv, const char* who) {
+  if (!kv) { set_error("%s: null handle", who); return OSCAR_E_ARG; }
+  if (kv->broken) {
+    set_error("%s: the handle is unusable after a HIP failure (destroy it and create a new store)", who);
+    return OSCAR_E_STATE;
+  }
+  return OSCAR_OK;
 }
 
 int check_desc(const oscar_kv_desc* d) {
@@ -125,7 +146,7 @@ int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd
         a.n = static_cast<int32_t>(std::min<size_t>(RUN_MAX, j - r));
         for (int k = 0; k < a.n; ++k) a.val[k] = upd[r + k].second;
         hipError_t e = launch_run(a, st);
-        if (e != hipSuccess) return hip_fail(e, "page-table update");
+        if (e != hipSuccess) return hip_fail_committed(kv, e, "page-table update");
       }
     } else {
       rest.insert(rest.end(), upd.begin() + i, upd.begin() + j);
@@ -141,7 +162,7 @@ int push_table(oscar_kv* kv, const std::vector<std::pair<int32_t, int32_t>>& upd
       a.val[k] = rest[i + k].second;
     }
     hipError_t e = launch_scatter(a, st);
-    if (e != hipSuccess) return hip_fail(e, "page-table update");
+    if (e != hipSuccess) return hip_fail_committed(kv, e, "page-table update");
   }
   return OSCAR_OK;
 }
@@ -231,8 +252,9 @@ size_t workspace_bytes_for(const oscar_kv* kv, int32_t n_seqs, const std::vector
 // Validation of a decode-step write (nothing is changed).
 int check_step_write(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
                      const char* who) {
-  if (!kv) { set_error("%s: null handle", who); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_usable(kv, who);
+  if (rc) return rc;
+  rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
   if (!kv->plan_only && (!k || !v)) { set_error("%s: null k or v", who); return OSCAR_E_ARG; }
   if (!kv->has_rotation) { set_error("%s: rotation not set", who); return OSCAR_E_STATE; }
@@ -304,8 +326,9 @@ StepArgs step_args(const oscar_kv* kv, const void* k, const void* v, const std::
 // Validation of a decode-attention call apart from its workspace size (nothing is changed).
 int check_decode(const oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* q, float sm_scale,
                  const float* out, const void* ws, const char* who) {
-  if (!kv) { set_error("%s: null handle", who); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_usable(kv, who);
+  if (rc) return rc;
+  rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
   if (!kv->plan_only && (!q || !out || !ws)) { set_error("%s: null q, out or workspace", who); return OSCAR_E_ARG; }
   if (!std::isfinite(sm_scale)) { set_error("%s: non-finite sm_scale", who); return OSCAR_E_ARG; }
@@ -423,6 +446,7 @@ void oscar_kv_destroy(oscar_kv* kv) { delete kv; }
 
 int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
   if (!kv || !rot_host) { set_error("oscar_kv_set_rotation: null argument"); return OSCAR_E_ARG; }
+  if (int rc = check_usable(kv, "oscar_kv_set_rotation")) return rc;
   const int hkv = kv->desc.num_kv_heads;
   const size_t n = static_cast<size_t>(hkv) * OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
   for (size_t i = 0; i < n; ++i)
@@ -469,8 +493,9 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
 
 int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t n_new, const void* k,
                    const void* v, void* stream) {
-  if (!kv) { set_error("oscar_kv_write: null handle"); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_usable(kv, "oscar_kv_write");
+  if (rc) return rc;
+  rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
   if (n_new < 1) { set_error("oscar_kv_write: n_new must be >= 1"); return OSCAR_E_ARG; }
   if (!kv->plan_only && (!k || !v)) { set_error("oscar_kv_write: null k or v"); return OSCAR_E_ARG; }
@@ -567,7 +592,7 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
     hipError_t e = t0 ? hipEventRecord(t0, st) : hipSuccess;
     if (e == hipSuccess) e = any_int2 ? launch_write(a, n_tiles, st) : launch_append(a, st);
     if (e == hipSuccess && t1) e = hipEventRecord(t1, st);
-    if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
+    if (e != hipSuccess) return hip_fail_committed(kv, e, "oscar_kv_write: launch");
   }
   // Writes that overflow a non-empty window, one sequence at a time: the tokens that fit, then
   // rounds of (evict the c oldest window tokens, append the next c tokens), c <= 256.  The c
@@ -610,7 +635,7 @@ int oscar_kv_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t
         a.seqs[0] = WriteSeq{w.seq, static_cast<int32_t>(len), 0, 0};
         e = launch_append(a, st);
       }
-      if (e != hipSuccess) return hip_fail(e, "oscar_kv_write: launch");
+      if (e != hipSuccess) return hip_fail_committed(kv, e, "oscar_kv_write: launch");
       len += c;
       t0 += c;
     }
@@ -631,8 +656,9 @@ int oscar_kv_set_write_evicts(oscar_kv* kv, int32_t on) {
 }
 
 int oscar_kv_evict_window(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, int32_t n_evict, void* stream) {
-  if (!kv) { set_error("oscar_kv_evict_window: null handle"); return OSCAR_E_ARG; }
-  int rc = check_seqs(kv, seq_ids, n_seqs);
+  int rc = check_usable(kv, "oscar_kv_evict_window");
+  if (rc) return rc;
+  rc = check_seqs(kv, seq_ids, n_seqs);
   if (rc) return rc;
   if (n_evict < 1) { set_error("oscar_kv_evict_window: n_evict must be >= 1"); return OSCAR_E_ARG; }
   const int64_t maxp = kv->desc.max_pages_per_seq;
@@ -682,7 +708,7 @@ int oscar_kv_evict_window(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, 
     a.n_seqs = std::min(CHUNK, n_seqs - c0);
     for (int i = 0; i < a.n_seqs; ++i) a.seqs[i] = plan[c0 + i];
     hipError_t e = launch_evict(a, st);
-    if (e != hipSuccess) return hip_fail(e, "oscar_kv_evict_window: launch");
+    if (e != hipSuccess) return hip_fail_committed(kv, e, "oscar_kv_evict_window: launch");
   }
   return OSCAR_OK;
 }
@@ -700,7 +726,7 @@ int oscar_kv_decode_write(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, 
   for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
     const StepArgs a = step_args(kv, k, v, plan, c0, std::min(CHUNK, n_seqs - c0));
     hipError_t e = launch_step_write(a, st);
-    if (e != hipSuccess) return hip_fail(e, "oscar_kv_decode_write: launch");
+    if (e != hipSuccess) return hip_fail_committed(kv, e, "oscar_kv_decode_write: launch");
   }
   return OSCAR_OK;
 }
@@ -762,11 +788,15 @@ int oscar_decode_step(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, cons
     for (int c0 = 0; c0 < n_seqs; c0 += CHUNK) {
       const StepArgs a = step_args(kv, k, v, plan, c0, std::min(CHUNK, n_seqs - c0));
       hipError_t e = launch_step_write(a, st);
-      if (e != hipSuccess) return hip_fail(e, "oscar_decode_step: launch");
+      if (e != hipSuccess) return hip_fail_committed(kv, e, "oscar_decode_step: launch");
     }
-    return launch_decode(kv, seq_ids, n_seqs, nullptr, q, sm_scale, out, ws, st, "oscar_decode_step");
+    rc = launch_decode(kv, seq_ids, n_seqs, nullptr, q, sm_scale, out, ws, st, "oscar_decode_step");
+    if (rc == OSCAR_E_HIP) kv->broken = true;
+    return rc;
   }
-  return launch_decode(kv, seq_ids, n_seqs, &plan, q, sm_scale, out, ws, st, "oscar_decode_step", k, v);
+  rc = launch_decode(kv, seq_ids, n_seqs, &plan, q, sm_scale, out, ws, st, "oscar_decode_step", k, v);
+  if (rc == OSCAR_E_HIP) kv->broken = true;
+  return rc;
 }
 
 int oscar_kv_seq_info(const oscar_kv* kv, int32_t seq, int64_t* len, int64_t* n_int2) {
@@ -791,6 +821,7 @@ int oscar_kv_free_pages(const oscar_kv* kv, int32_t* count, int32_t* host_out) {
 
 int oscar_kv_reset_seq(oscar_kv* kv, int32_t seq, void* stream) {
   if (!kv || seq < 0 || seq >= kv->desc.max_seqs) { set_error("oscar_kv_reset_seq: bad handle or seq"); return OSCAR_E_ARG; }
+  if (int rc = check_usable(kv, "oscar_kv_reset_seq")) return rc;
   const int64_t maxp = kv->desc.max_pages_per_seq;
   const int64_t pages = ceil_div(kv->n_int2[seq], kPage);
   std::vector<std::pair<int32_t, int32_t>> upd;

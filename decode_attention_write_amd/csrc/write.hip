@@ -55,7 +55,7 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 // so that all work-groups are resident at once (one residency round: no partial last round).
 //
 // Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_bf16.  The
-// A operand is R^T as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0) (|R - r0 - r1| <= 2^-18 |R|),
+// A operand is R^T as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0) (|R - r0 - r1| <= 2^-16 |R|),
 // the B operand the bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
 // its R^T operands in registers for all tiles of the work-group.
 
@@ -139,8 +139,13 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
     const int n_here = min(PAGE, a.n_new - tile * PAGE);
     const int p0 = sq.len0 + tile * PAGE;
     const int next = min(tile + 1, tile1 - 1);
-    // page of this tile (INT2 tiles only), fetched before the tile's work
-    const int page = (n_int2 > 0 && p0 >= SINK) ? ptab[tile - 1] : 0;
+    // INT2 destination: tokens j with SINK <= p0 + j < SINK + n_int2 (tile >= 1 of an empty
+    // sequence).  Only such a tile reads a page id, so the reads stay within the row's first
+    // ceil(n_int2 / 64) entries (tiles holding window tokens only read nothing); fetched before
+    // the tile's work.
+    int n_q = 0;
+    if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
+    const int page = (n_q > 0) ? ptab[tile - 1] : 0;
     stash(n_here, kreg);
     issue(a.k, next, kreg);
     __syncthreads();
@@ -191,9 +196,6 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       }
     }
 
-    // INT2 destination: tokens j with SINK <= p0 + j < SINK + n_int2 (tile >= 1 of an empty sequence)
-    int n_q = 0;
-    if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
     if (n_q > 0) {  // uniform across the block
       uint32_t* blk = reinterpret_cast<uint32_t*>(a.pool + (static_cast<size_t>(page) * a.hkv + kvh) * HEAD_BLOCK);
       // ranges and parameters: one (token j, group g) per thread, waves 0-1 keys, waves 2-3 values.

@@ -36,8 +36,13 @@
  *     and its mirror of the page table), never device memory.
  *   - Errors: every call returns OSCAR_OK (0) or a negative status.  A call
  *     that fails validation changes nothing; oscar_last_error() returns a
- *     message for the calling thread.  OSCAR_E_HIP (a launch failure) leaves
- *     the store undefined.  Faults inside kernels surface at the caller's next
+ *     message for the calling thread.  OSCAR_E_HIP (a HIP runtime call or launch
+ *     failed) from a call that changes the store (write, evict, decode-step
+ *     write, decode step, reset) comes after the call has moved its host
+ *     bookkeeping, so the device state may lag it: the handle is then marked
+ *     unusable and every later call on it returns OSCAR_E_STATE; destroy it and
+ *     create a new store.  OSCAR_E_HIP from oscar_decode_attn leaves the store
+ *     as it was.  Faults inside kernels surface at the caller's next
  *     synchronization.
  *   - One handle must not be used from two host threads at once.
  *
@@ -74,7 +79,8 @@ enum {
     OSCAR_E_NUMERIC = -5,       /* non-finite calibration input or eigensolver failure */
     OSCAR_E_HIP = -6,           /* a HIP runtime call or kernel launch failed */
     OSCAR_E_WORKSPACE = -7,     /* decode workspace smaller than oscar_decode_workspace_bytes */
-    OSCAR_E_STATE = -8          /* the call does not fit the sequence's state (e.g. empty sequence) */
+    OSCAR_E_STATE = -8          /* the call does not fit the sequence's state (e.g. empty sequence), or
+                                   the handle is unusable after an OSCAR_E_HIP */
 };
 
 /* Set in oscar_kv_desc.flags: keep every piece of host bookkeeping (page table
