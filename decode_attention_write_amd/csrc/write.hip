@@ -54,15 +54,22 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 // empty, tile i >= 1 holds INT2 indices 64 (i-1) ... = page i-1.  launch_write sizes the groups
 // so that all work-groups are resident at once (one residency round: no partial last round).
 //
-// Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_bf16.  The
-// A operand is R^T as two bf16 terms r0 = bf16(R), r1 = bf16(R - r0) (|R - r0 - r1| <= 2^-16 |R|),
-// the B operand the bf16 keys (exact), accumulation fp32.  Wave w owns output channels 32 w .. 32 w + 31 and keeps
-// its R^T operands in registers for all tiles of the work-group.
+// Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_f16.  The
+// A operand is S R^T (S = 2^14) as two fp16 terms r0 = fp16(S R^T), r1 = fp16(S R^T - r0), so
+// |S R^T - r0 - r1| <= 2^-22 |S R^T| (the scale keeps r1 out of the fp16 denormals); the B
+// operand is the key row scaled by a power of two 2^e that brings its largest magnitude into
+// [2^14, 2^15), which makes the bf16 -> fp16 conversion exact; the products are exact in fp32 and
+// accumulate in fp32; the result is multiplied by 2^-e / S (exact).  The rotated key is then
+// within about 2^-21 of sum_i |k_i R_ij| of the exact product, close to an fp32 dot product
+// (bf16 terms, 2^-16, moved the quantizer input enough to flip ring-key roundings and INT2 codes
+// measurably).  Wave w owns output channels 32 w .. 32 w + 31 and keeps its R^T operands in
+// registers for all tiles of the work-group.
 
 constexpr int XS = D + 4;  // fp32 row stride of the rotated tile (16-byte aligned rows)
-constexpr int KS = D + 8;  // bf16 row stride of the key tile
+constexpr int KS = D + 8;  // 16-bit row stride of the key / value tile
+constexpr float ROT_TERM_SCALE = 16384.0f;  // S: the fp16 terms hold S R^T
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h_w __attribute__((ext_vector_type(8)));
 typedef float v4f_w __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u_w __attribute__((ext_vector_type(4)));
 
@@ -77,22 +84,24 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
   const int len = sq.len0 + a.n_new;
   const int n_int2 = (sq.len0 == 0) ? max(0, len - RING) : 0;  // INT2 tokens of this call
 
-  // The tile buffer holds the bf16 keys (rotation input), then the bf16 values (quantizer input).
+  // The tile buffer holds the scaled fp16 keys (rotation input), then the bf16 values (quantizer
+  // input).
   __shared__ uint16_t tin[PAGE][KS];
+  __shared__ int kshift[PAGE];             // per key row of the tile: its fp16 scale exponent sh
   __shared__ float x[PAGE][XS];            // rotated keys, fp32
   // quantizer parameters per (token, K/V group 2 isv + g): fp32 minimum and reciprocal scale
   __shared__ float qlo[PAGE][4], qinv[PAGE][4];
 
-  // A operands: R^T rows of this wave's output channels, 4 K-steps of 32 input channels, 2 terms
+  // A operands: S R^T rows of this wave's output channels, 4 K-steps of 32 input channels, 2 terms
   const uint16_t* terms = reinterpret_cast<const uint16_t*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES + D * D * 4);
-  v8bf aop[2][4][2];
+  v8h_w aop[2][4][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        aop[mt][ks][t] = *reinterpret_cast<const v8bf*>(terms + t * D * D + (32 * wave + 16 * mt + n16) * D + 32 * ks + 8 * q4);
+        aop[mt][ks][t] = *reinterpret_cast<const v8h_w*>(terms + t * D * D + (32 * wave + 16 * mt + n16) * D + 32 * ks + 8 * q4);
 
   const size_t row = static_cast<size_t>(a.hkv) * D;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
@@ -129,6 +138,41 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       }
     }
   };
+  // Keys go to LDS as raw bf16 (stash) and are then converted in place to fp16, each row scaled by
+  // the power of two 2^sh that puts its largest magnitude in [2^14, 2^15) (exact: a bf16 value has
+  // 8 significant bits, and every entry within 2^-24 of the row's largest stays an fp16 normal;
+  // smaller ones round to the fp16 denormal grid, an error below 2^-39 of the row's largest).
+  // The conversion is a pass over LDS after a barrier, so that no extra registers are live while
+  // the next tile's loads are in flight; the 16 threads of a row combine their largest
+  // magnitudes with DPP row operations (xor 1, xor 2, half-row mirror, row mirror).
+  auto keys_to_f16 = [&]() {
+#pragma unroll 2
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r, j = i >> 4;
+      v4u_w* cell = reinterpret_cast<v4u_w*>(&tin[j][8 * (i & 15)]);
+      const v4u_w w = *cell;
+      uint32_t mb = 0;   // largest |bf16| as bits (the bit patterns order like the magnitudes)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mb = max(mb, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+      mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0xB1, 0xF, 0xF, false)));
+      mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0x4E, 0xF, 0xF, false)));
+      mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0x141, 0xF, 0xF, false)));
+      mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0x140, 0xF, 0xF, false)));
+      // exponent of the largest magnitude (bf16 exponent field, bias 127); all-zero rows keep 0
+      const int ex = (mb >= 0x0080u) ? static_cast<int>(mb >> 7) - 127 : (mb ? -126 : 14);
+      const int sh = 14 - ex;
+      if ((i & 15) == 0) kshift[j] = sh;
+      v4u_w h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = __builtin_ldexpf(__uint_as_float(w[e] << 16), sh);
+        const float k1 = __builtin_ldexpf(__uint_as_float(w[e] & 0xFFFF0000u), sh);
+        h[e] = static_cast<uint32_t>(__half_as_ushort(__float2half_rn(k0))) |
+               (static_cast<uint32_t>(__half_as_ushort(__float2half_rn(k1))) << 16);
+      }
+      *cell = h;
+    }
+  };
   // page ids through the scalar cache (the table is not written by this kernel)
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(sq.seq) * a.max_pages);
@@ -149,21 +193,25 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
     stash(n_here, kreg);
     issue(a.k, next, kreg);
     __syncthreads();
+    keys_to_f16();
+    __syncthreads();
 
-    // rotation: 16-token column tiles; each (output tile, K-step) takes the two R^T terms
+    // rotation: 16-token column tiles; each (output tile, K-step) takes the two S R^T terms; the
+    // accumulators of token 16 nt + n16 are unscaled by that row's 2^-e / S
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      v8bf b[4];
+      v8h_w b[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const v8bf*>(&tin[16 * nt + n16][32 * ks + 8 * q4]);
+      for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const v8h_w*>(&tin[16 * nt + n16][32 * ks + 8 * q4]);
+      const float sc = __builtin_ldexpf(1.0f / ROT_TERM_SCALE, -kshift[16 * nt + n16]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         v4f_w acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int t = 1; t >= 0; --t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt][ks][t], b[ks], acc, 0, 0, 0);
-        *reinterpret_cast<v4f_w*>(&x[16 * nt + n16][32 * wave + 16 * mt + 4 * q4]) = acc;
+          for (int t = 1; t >= 0; --t) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[mt][ks][t], b[ks], acc, 0, 0, 0);
+        *reinterpret_cast<v4f_w*>(&x[16 * nt + n16][32 * wave + 16 * mt + 4 * q4]) = acc * sc;
       }
     }
     __syncthreads();
@@ -178,7 +226,11 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       // trip count around the stores would make every later wait on the prefetch a full drain)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = tid + 256 * r, j = i >> 4, c8 = 8 * (i & 15), p = p0 + j;
+        // the thread index passes through an empty asm so that the compiler derives these
+        // addresses here instead of keeping them live across the loop (they spilled)
+        int t_ = tid;
+        asm volatile("" : "+v"(t_));
+        const int i = t_ + 256 * r, j = i >> 4, c8 = 8 * (i & 15), p = p0 + j;
         const bool int2 = (p >= SINK) && (p < SINK + n_int2);
         if (j < n_here && !int2) {
           const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;

@@ -70,7 +70,7 @@ def _check_state(gpu, ora, seqs, rot, inputs):
     gpool, gring, gtable = gpu
     assert np.array_equal(gtable, ora.page_table)
     totals = dict(elements=0, code_mismatch=0, unexplained=0, k_meta_flips=0, v_meta_flips=0, meta_far=0,
-                  groups=0, tail_nonzero=0, k_meta_unexplained=0)
+                  groups=0, tail_nonzero=0, k_meta_unexplained=0, explained_by_meta=0)
     k_ulp_flips = 0
     for s in seqs:
         L, n2 = int(ora.length[s]), int(ora.n_int2[s])
@@ -125,6 +125,25 @@ def test_generator_gpu_twin_bit_exact(gpu_lib):
     for h in range(hkv):
         kr, vr = synth.unit_kv(synth.CFG_QWEN3_4B, 5, 4, h, n, t0)
         assert np.array_equal(kh[:, h], kr) and np.array_equal(vh[:, h], vr)
+
+
+def test_rotation_blob_terms(gpu_lib):
+    """The device rotation block of each KV head: fp32 R, then fp16 r0 = fp16(2^14 R^T) and
+    r1 = fp16(2^14 R^T - r0) (round to nearest even; numpy's conversions), then a zero slot."""
+    _case("rotation blob")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 3, 2)
+    st = _store(gpu_lib, 8, 2, 1, 4, 4, None, rot)
+    import torch
+    torch.cuda.synchronize()
+    blob = st.rot.cpu().numpy().reshape(2, -1)
+    for h in range(2):
+        assert np.array_equal(blob[h, :65536].view(np.float32).reshape(128, 128), rot[h])
+        rs = rot[h].T.astype(np.float32) * np.float32(16384)
+        r0 = rs.astype(np.float16)
+        r1 = (rs - r0.astype(np.float32)).astype(np.float16)
+        terms = blob[h, 65536:].view(np.uint16).reshape(3, 128, 128)
+        assert np.array_equal(terms[0], r0.view(np.uint16)) and np.array_equal(terms[1], r1.view(np.uint16))
+        assert not terms[2].any()
 
 
 def test_tiny_config_write_and_decode(gpu_lib):
