@@ -43,8 +43,9 @@ EXPORTS = [
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
     "oscar_decode_step_workspace_bytes", "oscar_decode_step", "oscar_kv_set_write_evicts",
-    "oscar_kv_set_output_bf16",
+    "oscar_kv_set_output_bf16", "oscar_decode_step_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20   # OSCAR_NOALLOC_SCRATCH_BYTES
 
 
 class OscarError(RuntimeError):
@@ -98,6 +99,7 @@ def load():
         "oscar_decode_step": [P, P, I32, P, P, P, ctypes.c_float, P, P, SZ, P],
         "oscar_kv_set_write_evicts": [P, I32],
         "oscar_kv_set_output_bf16": [P, I32],
+        "oscar_decode_step_noalloc": [P, P, I32, P, P, P, ctypes.c_float, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -281,6 +283,22 @@ def oscar_decode_step(store, seq_ids, k, v, q, sm_scale, out, ws, stream=None):
                                     _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
+def oscar_decode_step_noalloc(store, seq_ids, k, v, q, sm_scale, out, stream=None):
+    """oscar_decode_step with the workspace taken from the library's per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES): allocates nothing.  Calls that overlap on one GPU race."""
+    ids, p = _i32(seq_ids)
+    if store.plan_only:
+        _check(load().oscar_decode_step_noalloc(store.handle, p, len(ids), None, None, None, ctypes.c_float(sm_scale),
+                                                None, None))
+        return
+    for t, name in ((k, "k"), (v, "v")):
+        check_tensor(t, name, (len(ids), store.hkv, HEAD_DIM), _bf16_types(), store.device)
+    check_tensor(q, "q", (len(ids), store.hq, HEAD_DIM), _bf16_types(), store.device)
+    check_tensor(out, "out", (len(ids), store.hq, HEAD_DIM), _out_types(store), store.device)
+    _check(load().oscar_decode_step_noalloc(store.handle, p, len(ids), _ptr(k), _ptr(v), _ptr(q),
+                                            ctypes.c_float(sm_scale), _ptr(out), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------- store object
 
 class KVStore:
@@ -384,6 +402,12 @@ class KVStore:
             import torch
             ws = torch.empty(max(4, self.step_workspace_bytes(seq_ids)) // 4, dtype=torch.float32, device=q.device)
         oscar_decode_step(self, seq_ids, k, v, q, sm_scale, out, ws, stream)
+        return out
+
+    def decode_step_noalloc(self, seq_ids, k, v, q, sm_scale, out, stream=None):
+        """decode_step with the library's scratch array instead of a workspace; `out` is required
+        (this form allocates nothing)."""
+        oscar_decode_step_noalloc(self, seq_ids, k, v, q, sm_scale, out, stream)
         return out
 
     def seq_info(self, seq):

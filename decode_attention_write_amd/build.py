@@ -28,6 +28,7 @@ SOURCES = {
     "calibrate.cpp": [],
     "write.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "scratch.hip": [],
     # keep MFMA accumulators in arch VGPRs (no AGPR copies around the running rescale)
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

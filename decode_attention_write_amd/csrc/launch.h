@@ -155,6 +155,10 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // work-groups of the decode split kernel to plan per residency round on the current device
 int decode_resident_workgroups(int gqa, int kernel);
 
+// Address of the allocation-free decode step's scratch array on the current device (looked up once
+// per device with hipGetSymbolAddress, then cached); OSCAR_NOALLOC_SCRATCH_BYTES bytes.
+hipError_t scratch_on_current_device(void** ptr);
+
 // bytes of the prepared-query area that follows the split partials in the workspace,
 // per (sequence of a launch chunk, KV head)
 constexpr int QPREP_STRIDE = 8448;

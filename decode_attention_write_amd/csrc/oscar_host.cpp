@@ -829,6 +829,26 @@ int oscar_decode_step(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, cons
   return rc;
 }
 
+int oscar_decode_step_noalloc(oscar_kv* kv, const int32_t* seq_ids, int32_t n_seqs, const void* k, const void* v,
+                              const void* q, float sm_scale, float* out, void* stream) {
+  int rc = check_step_write(kv, seq_ids, n_seqs, k, v, "oscar_decode_step_noalloc");
+  if (rc) return rc;
+  size_t need = 0;
+  rc = oscar_decode_step_workspace_bytes(kv, seq_ids, n_seqs, &need);
+  if (rc) return rc;
+  if (need > OSCAR_NOALLOC_SCRATCH_BYTES) {
+    set_error("oscar_decode_step_noalloc: the step needs %zu bytes of scratch > %u (use oscar_decode_step with a "
+              "workspace)", need, OSCAR_NOALLOC_SCRATCH_BYTES);
+    return OSCAR_E_WORKSPACE;
+  }
+  void* ws = nullptr;  // plan-only stores enqueue nothing and take no workspace
+  if (!kv->plan_only) {
+    const hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess) return hip_fail(e, "oscar_decode_step_noalloc: scratch address");
+  }
+  return oscar_decode_step(kv, seq_ids, n_seqs, k, v, q, sm_scale, out, ws, OSCAR_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int oscar_kv_seq_info(const oscar_kv* kv, int32_t seq, int64_t* len, int64_t* n_int2) {
   if (!kv || seq < 0 || seq >= kv->desc.max_seqs) { set_error("oscar_kv_seq_info: bad handle or seq"); return OSCAR_E_ARG; }
   if (len) *len = kv->len[seq];

@@ -324,6 +324,25 @@ int oscar_decode_step_workspace_bytes(const oscar_kv *kv, const int32_t *seq_ids
 int oscar_decode_step(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *k, const void *v,
                       const void *q, float sm_scale, float *out, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * oscar_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the step's split partials, prepared queries
+ * and page-group counters live in a device array inside the library,
+ * OSCAR_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the library's load until
+ * the process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); its first call on a device looks the array's address up.
+ * Arguments, results and errors as oscar_decode_step; OSCAR_E_WORKSPACE when
+ * the step needs more than OSCAR_NOALLOC_SCRATCH_BYTES (what
+ * oscar_decode_step_workspace_bytes reports), OSCAR_E_HIP when the array's
+ * address cannot be looked up (nothing is changed then).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, two
+ * threads, two handles) race and must be ordered by the caller.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+int oscar_decode_step_noalloc(oscar_kv *kv, const int32_t *seq_ids, int32_t n_seqs, const void *k,
+                              const void *v, const void *q, float sm_scale, float *out, void *stream);
+
 /* Length and INT2 token count of one sequence. */
 int oscar_kv_seq_info(const oscar_kv *kv, int32_t seq, int64_t *len, int64_t *n_int2);
 

@@ -375,3 +375,22 @@ def test_binding_rejects_mismatched_tensors():
             oscar.check_tensor(t, "k", (2, 3, 4, 128), (torch.int16, torch.bfloat16))
     with pytest.raises(ValueError, match="on cpu"):
         oscar.check_tensor(ok, "k", (2, 3, 4, 128), (torch.int16,), torch.device("meta"))
+
+
+def test_noalloc_step_host_limits():
+    """The allocation-free decode step plans like the workspace form and refuses a step whose
+    workspace would exceed the library's scratch array (plan-only store, host logic)."""
+    hkv, hq, B, L = 8, 64, 64, 320 + 64 * 11
+    st = oscar.KVStore(hq, hkv, B, 12, B * 12, plan_only=True)
+    st.set_rotation(np.stack([np.eye(128, dtype=np.float32)] * hkv))
+    ids = list(range(B))
+    st.write(ids, None, None, n_new=L)
+    st.set_decode_split(1)
+    assert st.step_workspace_bytes(ids) > oscar.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(oscar.OscarError, match="E_WORKSPACE"):
+        oscar.oscar_decode_step_noalloc(st, ids, None, None, None, 0.1, None)
+    assert st.seq_info(0) == (L, L - 320)                      # nothing changed
+    st.set_decode_split(0)
+    assert st.step_workspace_bytes(ids[:4]) <= oscar.NOALLOC_SCRATCH_BYTES
+    oscar.oscar_decode_step_noalloc(st, ids[:4], None, None, None, 0.1, None)
+    assert st.seq_info(0) == (L + 1, L - 320 + 1)              # the step's write was planned
