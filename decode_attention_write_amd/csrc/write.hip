@@ -7,6 +7,7 @@
 // token to asymmetric INT2 in 64-channel groups; recent tokens stay BF16
 // (section "Together AI, INT2 KV 캐시 시스템 'OSCAR' 공개").
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "step_write.h"
@@ -57,9 +58,9 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 // Rotation on the matrix cores, transposed: x^T = R^T k^T with v_mfma_f32_16x16x32_f16.  The
 // A operand is S R^T (S = 2^14) as two fp16 terms r0 = fp16(S R^T), r1 = fp16(S R^T - r0), so
 // |S R^T - r0 - r1| <= 2^-22 |S R^T| (the scale keeps r1 out of the fp16 denormals); the B
-// operand is the key row scaled by a power of two 2^e that brings its largest magnitude into
+// operand is the key row scaled by a power of two 2^sh that brings its largest magnitude into
 // [2^14, 2^15), which makes the bf16 -> fp16 conversion exact; the products are exact in fp32 and
-// accumulate in fp32; the result is multiplied by 2^-e / S (exact).  The rotated key is then
+// accumulate in fp32; the result is multiplied by 2^-sh / S (exact).  The rotated key is then
 // within about 2^-21 of sum_i |k_i R_ij| of the exact product, close to an fp32 dot product
 // (bf16 terms, 2^-16, moved the quantizer input enough to flip ring-key roundings and INT2 codes
 // measurably).  Wave w owns output channels 32 w .. 32 w + 31 and keeps its R^T operands in
@@ -70,6 +71,7 @@ constexpr int KS = D + 8;  // 16-bit row stride of the key / value tile
 constexpr float ROT_TERM_SCALE = 16384.0f;  // S: the fp16 terms hold S R^T
 
 typedef _Float16 v8h_w __attribute__((ext_vector_type(8)));
+typedef unsigned short v2us_w __attribute__((ext_vector_type(2)));
 typedef float v4f_w __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u_w __attribute__((ext_vector_type(4)));
 
@@ -124,12 +126,7 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
   // Register -> LDS.  The rows past the call's tokens are then overwritten with zeros (LDS stores
   // only: selecting in registers let the compiler hoist the select, and with it the wait on the
   // loads, above the rotation).
-  auto stash = [&](int nh, const v4u_w* w) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = tid + 256 * r;
-      *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = w[r];
-    }
+  auto stash_tail = [&](int nh) {
     if (nh < PAGE) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -138,22 +135,29 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       }
     }
   };
-  // Keys go to LDS as raw bf16 (stash) and are then converted in place to fp16, each row scaled by
-  // the power of two 2^sh that puts its largest magnitude in [2^14, 2^15) (exact: a bf16 value has
-  // 8 significant bits, and every entry within 2^-24 of the row's largest stays an fp16 normal;
-  // smaller ones round to the fp16 denormal grid, an error below 2^-39 of the row's largest).
-  // The conversion is a pass over LDS after a barrier, so that no extra registers are live while
-  // the next tile's loads are in flight; the 16 threads of a row combine their largest
-  // magnitudes with DPP row operations (xor 1, xor 2, half-row mirror, row mirror).
-  auto keys_to_f16 = [&]() {
-#pragma unroll 2
+  auto stash = [&](int nh, const v4u_w* w) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = tid + 256 * r;
+      *reinterpret_cast<v4u_w*>(&tin[i >> 4][8 * (i & 15)]) = w[r];
+    }
+    stash_tail(nh);
+  };
+  // Keys go to LDS as fp16, each row (token) scaled by the power of two 2^sh that puts its largest
+  // magnitude in [2^14, 2^15): exact, since a bf16 value has 8 significant bits and every entry
+  // within 2^-28 of the row's largest is then an fp16 normal; smaller ones round to the fp16
+  // denormal grid, an error below 2^-39 of the row's largest.  The conversion happens once, in
+  // the registers the tile was loaded into, before they go to LDS: the 16 threads of a row take
+  // the largest magnitude of their 8 values with packed 16-bit maxima, then combine them with
+  // DPP row operations (xor 1, xor 2, half-row mirror, row mirror).  sh goes to LDS per row.
+  auto stash_keys = [&](int nh, v4u_w* w) {
+#pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = tid + 256 * r, j = i >> 4;
-      v4u_w* cell = reinterpret_cast<v4u_w*>(&tin[j][8 * (i & 15)]);
-      const v4u_w w = *cell;
-      uint32_t mb = 0;   // largest |bf16| as bits (the bit patterns order like the magnitudes)
+      v2us_w m2 = __builtin_bit_cast(v2us_w, w[r][0] & 0x7FFF7FFFu);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mb = max(mb, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+      for (int e = 1; e < 4; ++e) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(v2us_w, w[r][e] & 0x7FFF7FFFu));
+      uint32_t mb = max(static_cast<uint32_t>(m2.x), static_cast<uint32_t>(m2.y));
       mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0xB1, 0xF, 0xF, false)));
       mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0x4E, 0xF, 0xF, false)));
       mb = max(mb, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(mb), 0x141, 0xF, 0xF, false)));
@@ -162,16 +166,16 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       const int ex = (mb >= 0x0080u) ? static_cast<int>(mb >> 7) - 127 : (mb ? -126 : 14);
       const int sh = 14 - ex;
       if ((i & 15) == 0) kshift[j] = sh;
-      v4u_w h;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float k0 = __builtin_ldexpf(__uint_as_float(w[e] << 16), sh);
-        const float k1 = __builtin_ldexpf(__uint_as_float(w[e] & 0xFFFF0000u), sh);
-        h[e] = static_cast<uint32_t>(__half_as_ushort(__float2half_rn(k0))) |
-               (static_cast<uint32_t>(__half_as_ushort(__float2half_rn(k1))) << 16);
+        const uint32_t u = w[r][e];
+        const _Float16 h0 = static_cast<_Float16>(__builtin_ldexpf(__uint_as_float(u << 16), sh));
+        const _Float16 h1 = static_cast<_Float16>(__builtin_ldexpf(__uint_as_float(u & 0xFFFF0000u), sh));
+        w[r][e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
       }
-      *cell = h;
     }
+    stash(nh, w);
   };
   // page ids through the scalar cache (the table is not written by this kernel)
   const __attribute__((address_space(4))) int32_t* ptab =
@@ -190,14 +194,12 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
     int n_q = 0;
     if (n_int2 > 0 && p0 >= SINK) n_q = max(0, min(n_here, SINK + n_int2 - p0));
     const int page = (n_q > 0) ? ptab[tile - 1] : 0;
-    stash(n_here, kreg);
+    stash_keys(n_here, kreg);
     issue(a.k, next, kreg);
-    __syncthreads();
-    keys_to_f16();
     __syncthreads();
 
     // rotation: 16-token column tiles; each (output tile, K-step) takes the two S R^T terms; the
-    // accumulators of token 16 nt + n16 are unscaled by that row's 2^-e / S
+    // accumulators of token 16 nt + n16 are unscaled by that row's 2^-sh / S
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       v8h_w b[4];
@@ -254,7 +256,9 @@ __global__ __launch_bounds__(256, 3) void k_write(WriteArgs a) {
       // The group's 64 values are read in 16-byte pieces; rows of consecutive lanes fall in
       // distinct banks.
       {
-        const int j = tid & 63, g = (tid >> 6) & 1, isv = tid >> 7;
+        int t_ = tid;                 // opaque copy: keeps these LDS addresses out of the loop's
+        asm volatile("" : "+v"(t_));  // live registers (they spilled when hoisted)
+        const int j = t_ & 63, g = (t_ >> 6) & 1, isv = t_ >> 7;
         float lo = 0.0f, inv = 0.0f;
         uint32_t mword = 0u;
         if (j < n_q) {

@@ -343,6 +343,40 @@ def test_degenerate_and_extreme_groups(gpu_lib):
     assert parity.rel_l2(out, iso) <= ISO_TOL
 
 
+def test_keys_outside_fp16_range(gpu_lib):
+    """Keys that fp16 does not represent exactly (entries >= 2^16, rows of values below 2^-14, rows
+    mixing both scales) make the write kernel scale each key row by a power of two before its
+    fp16 rotation: stored state under the tolerance rules (key-metadata flips explained by the
+    rotation error) with a calibrated rotation, and decode parity on identical state."""
+    hkv, hq = 2, 8
+    L = 320 + 64 * 3 + 5
+    _case("keys outside the fp16 range (scaled rotation path)")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 10, hkv)
+    rng = np.random.default_rng(17)
+    k = rng.standard_normal((L, hkv, D)).astype(np.float32)
+    for t in range(L):
+        kind = t % 5
+        if kind == 1:
+            k[t, :, t % D] = 7.0e4 * (1 if t % 2 else -1)         # one entry above 2^16
+        elif kind == 2:
+            k[t] *= 1e-6                                          # a row below 2^-14
+        elif kind == 3:
+            k[t, :, ::2] *= 1e4                                   # 1e4 beside values near 1 ...
+            k[t, :, 1::4] *= 1e-7                                 # ... and values near 1e-7
+    kb = synth.f32_to_bf16_bits(k)
+    vb = synth.f32_to_bf16_bits(rng.standard_normal((L, hkv, D)).astype(np.float32))
+    st = _store(gpu_lib, hq, hkv, 1, 8, 8, None, rot)
+    ora = ostore.OracleStore(hkv, 1, 8, 8, range(8), rot)
+    st.write([0], parity.to_dev_bf16(kb[None]), parity.to_dev_bf16(vb[None]))
+    ora.write([0], kb[None], vb[None])
+    gpu = parity.export(st)
+    _check_state(gpu, ora, [0], rot, {0: (kb, vb, L)})
+    q = synth.decode_queries(synth.CFG_QWEN3_4B, 10, 1, hq, hkv)
+    out = st.decode([0], parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, [0], SCALE, hq)
+    assert np.all(np.isfinite(out)) and parity.rel_l2(out, iso) <= ISO_TOL
+
+
 def test_more_sequences_than_one_launch(gpu_lib):
     """70 sequences (a launch takes at most 64): one batched first write, then three one-call decode
     steps (each evicting, pages crossing at INT2 index 128) and an attention call, all with the
