@@ -104,71 +104,145 @@ def export_units(st, seqs_kv):
     return out
 
 
-def _cpu_unit(job):
-    """One (seq, kv head) unit of the oracle's decode attention in a worker process (no GPU use):
-    returns its decode time and output."""
+def _cpu_job(job):
+    """One sampled unit of CPU-oracle work in a worker process (no GPU use), single-threaded BLAS.
+    Returns (seconds of the timed part, output or None).  Jobs:
+      ("warm",)                                        imports only
+      ("decode", L, n2, pool_u, ring_u, rot, q, g)     decode attention of one (seq, KV head)
+                                                       unit on its exported store state
+      ("write", cfg, layer, seq, kv, n, rot1)          first write of n tokens into an empty
+                                                       one-head store (inputs drawn untimed)
+      ("appends", cfg, layer, seq, kv, L, n, rot1)     n single-token decode-step writes (evict
+                                                       when the window is full, append) after an
+                                                       untimed first write of L tokens
+    """
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
         threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         pass
-    from oracle import attention
-    L, n2, pool_u, ring_u, rot, q, g = job
-    if pool_u is None:
-        return 0.0, None          # warm-up task: imports only
-    table_u = np.arange(pool_u.shape[0], dtype=np.int32)[None, :]
-    t1 = time.perf_counter()
-    out = attention.decode(pool_u, ring_u, table_u, np.array([L]), np.array([n2]), rot, q, [0], 1 / math.sqrt(128), g)
-    return time.perf_counter() - t1, out
+    import synth
+    from oracle import attention, store as ostore
+    kind = job[0]
+    if kind == "warm":
+        return 0.0, None
+    if kind == "decode":
+        _, L, n2, pool_u, ring_u, rot, q, g = job
+        table_u = np.arange(pool_u.shape[0], dtype=np.int32)[None, :]
+        t1 = time.perf_counter()
+        out = attention.decode(pool_u, ring_u, table_u, np.array([L]), np.array([n2]), rot, q, [0],
+                               1 / math.sqrt(128), g)
+        return time.perf_counter() - t1, out
+    if kind == "write":
+        _, cfg, layer, seq, kv, n, rot1 = job
+        kb, vb = synth.unit_kv(cfg, layer, seq, kv, n)
+        pages = -(-max(0, n - 320) // 64) + 1
+        st = ostore.OracleStore(1, 1, pages, pages, range(pages), rot1)
+        t1 = time.perf_counter()
+        st.write([0], kb[None, :, None, :], vb[None, :, None, :])
+        return time.perf_counter() - t1, None
+    if kind == "appends":
+        _, cfg, layer, seq, kv, L, n, rot1 = job
+        kb, vb = synth.unit_kv(cfg, layer, seq, kv, L + n)
+        pages = -(-(L + n) // 64) + 1
+        st = ostore.OracleStore(1, 1, pages, pages, range(pages), rot1)
+        st.write([0], kb[None, :L, None, :], vb[None, :L, None, :])
+        t1 = time.perf_counter()
+        for i in range(L, L + n):
+            if st.window_count(0) == 256:
+                st.evict([0], 1)
+            st.write([0], kb[None, i:i + 1, None, :], vb[None, i:i + 1, None, :])
+        return time.perf_counter() - t1, None
+    raise ValueError(kind)
 
 
-def cpu_baseline(units, rots, q_layer0, out_layer0, hq, hkv, total_units, step_bytes_attn):
-    """Time the oracle's decode attention on sampled (layer 0, seq, kv head) units on the host's
-    cores: P worker processes (spawned, one BLAS thread each, P = min(16, cores available)) run
-    the units concurrently; each unit's decode time is measured inside its worker.  The step's
-    CPU time is extrapolated as total units x mean unit time / P.
+def host_info():
+    """CPU model and the NumPy/BLAS thread settings of this process."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{k: d.get(k) for k in ("internal_api", "version", "num_threads")} for d in threadpool_info()]
+    except Exception:  # pragma: no cover
+        pass
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    return model, blas, env
 
-    The oracle runs on the GPU's exported store state of each unit (identical inputs), so the
-    reported rel-L2 is the decode parity figure.
+
+def cpu_baseline(legs):
+    """Time the oracle, as it stands, on sampled units of each workload on the host's cores.
+
+    legs: {name: (jobs, extrapolate)}; extrapolate(times, outputs, P) returns the leg's report.
+    All jobs run on P spawned worker processes (P = min(16, cores available), one BLAS thread
+    each; each job's time is measured inside its worker).  The leg "c2_decode" (decode attention
+    of the 100000-token x 32-sequence step on the GPU's exported store of each sampled unit) is
+    the reported `value`; the others go under "legs".
     """
     import multiprocessing as mp
-    import numpy as np
     if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         raise RuntimeError("the CPU-oracle leg spawns worker processes: run it outside the profiler "
                            "(profiled runs take --no-cpu-baseline)")
-    g = hq // hkv
-    P = max(1, min(16, len(os.sched_getaffinity(0)), len(units)))
-    jobs = [(L, n2, pool_u, ring_u, rots[0][kv:kv + 1], q_layer0[s:s + 1, kv * g:(kv + 1) * g], g)
-            for s, kv, L, n2, pool_u, ring_u in units]
+    P = max(1, min(16, len(os.sched_getaffinity(0))))
+    names = list(legs)
+    flat = [(n, j) for n in names for j in legs[n][0]]
     with mp.get_context("spawn").Pool(P) as pool:
-        pool.map(_cpu_unit, [(0, 0, None, None, None, None, g)] * P, chunksize=1)   # start-up, not timed
+        pool.map(_cpu_job, [("warm",)] * P, chunksize=1)   # start-up, not timed
         w0 = time.perf_counter()
-        res = pool.map(_cpu_unit, jobs, chunksize=1)
+        res = pool.map(_cpu_job, [j for _, j in flat], chunksize=1)
         wall = time.perf_counter() - w0
-    times = [t for t, _ in res]
-    errs = []
-    for (s, kv, L, n2, _, _), (t, out) in zip(units, res):
-        gpu = out_layer0[s, kv * g:(kv + 1) * g]
-        errs.append(float(np.linalg.norm(gpu - out[0]) / np.linalg.norm(out[0])))
-    per_unit = float(np.mean(times))
-    cpu_step_s = per_unit * total_units / P
-    log(f"cpu oracle: {len(units)} units on {P} worker processes in {wall:.1f} s wall, "
-        f"{per_unit:.2f} s per unit, max rel-l2 vs gpu {max(errs):.2e}")
-    return {
-        "value": step_bytes_attn / cpu_step_s / 1e9,
-        "unit": "GB/s",
-        "cores": P,
-        "kind": "oracle",
-        "sample": (f"{len(units)} of {total_units} (layer, seq, kv-head) units of the attention pass "
-                   f"(oracle on the GPU's exported store of each unit, 100000-token context), decode "
-                   f"attention only, on {P} concurrent single-threaded worker processes, "
-                   f"extrapolated x{total_units}/{P}"),
-        "seconds_per_unit": per_unit,
-        "cpu_seconds_sampled": float(np.sum(times)),
-        "value_one_core": step_bytes_attn / (per_unit * total_units) / 1e9,
-        "sample_rel_l2_vs_gpu": max(errs),
-    }
+    by = {n: ([], []) for n in names}
+    for (n, _), (t, out) in zip(flat, res):
+        by[n][0].append(t)
+        by[n][1].append(out)
+    reports = {n: legs[n][1](by[n][0], by[n][1], P) for n in names}
+    head = reports.pop("c2_decode")
+    model, blas, env = host_info()
+    cpu_s = float(sum(t for n in names for t in by[n][0]))
+    log(f"cpu oracle: {len(flat)} sampled jobs on {P} worker processes in {wall:.1f} s wall ({cpu_s:.1f} s CPU); "
+        f"step attention {head['value']:.3f} GB/s; max rel-l2 vs gpu {head['sample_rel_l2_vs_gpu']:.2e}")
+    head.update({"cores": P, "kind": "oracle", "cpu_model": model, "blas": blas, "blas_env": env,
+                 "worker_blas_threads": 1, "cpu_seconds_all_legs": round(cpu_s, 2),
+                 "wall_seconds_all_legs": round(wall, 2), "legs": reports})
+    return head
+
+
+def decode_leg(st, seqs_kv, rot, q_host, gpu_out, hq, hkv, label, n_layers=1):
+    """CPU-oracle leg of decode attention: jobs for the sampled (seq, KV head) units on their
+    exported store state, and the report builder.  The workload (n_layers layers of this store's
+    state) takes the sampled units' time scaled by its split-kernel bytes over the sampled units'
+    bytes, run on P cores; its rate counts the decode call's algorithmic bytes.  The sampled
+    outputs are compared with the GPU's (gpu_out: the store's decode output on the same state)."""
+    import numpy as np
+    g = hq // hkv
+    units = export_units(st, seqs_kv)
+    jobs = [("decode", L, n2, pool_u, ring_u, rot[kv:kv + 1], q_host[s:s + 1, kv * g:(kv + 1) * g], g)
+            for s, kv, L, n2, pool_u, ring_u in units]
+    info = [st.seq_info(s) for s in range(len(gpu_out))]
+    lens, n2s = [L for L, _ in info], [n2 for _, n2 in info]
+    scale_total = n_layers * split_kernel_bytes(lens, n2s, hkv)
+    value_total = n_layers * decode_bytes(lens, n2s, hq, hkv)
+    sample = sum(split_kernel_bytes([L], [n2], 1) for _, _, L, n2, _, _ in units)
+    n_units = n_layers * len(lens) * hkv
+
+    def rep(times, outs, P):
+        cpu_total = float(np.sum(times)) * scale_total / sample
+        errs = [float(np.linalg.norm(gpu_out[s, kv * g:(kv + 1) * g] - o[0]) / np.linalg.norm(o[0]))
+                for (s, kv), o in zip(seqs_kv, outs)]
+        return {"value": value_total / (cpu_total / P) / 1e9, "unit": "GB/s", "workload": label,
+                "sample": f"{len(times)} of {n_units} (seq, kv-head) units, decode attention on the GPU's "
+                          f"exported store state, scaled by bytes ({scale_total / sample:.1f}x) over {P} cores",
+                "seconds_sampled": round(float(np.sum(times)), 3), "seconds_on_P_cores": round(cpu_total / P, 3),
+                "value_one_core": value_total / cpu_total / 1e9, "sample_rel_l2_vs_gpu": max(errs)}
+    return jobs, rep
 
 
 PREFILL_TOKENS, PREFILL_APPENDS = 131072, 1024
@@ -183,9 +257,13 @@ def prefill_bytes(n_tokens, hkv):
     return hkv * (512 * n_tokens + 80 * n_int2 + 512 * n_bf16) + 4 * (-(-n_int2 // 64))
 
 
-def prefill_leg(reps=5):
+CPU_APPEND_SAMPLE = (4096, 256)    # oracle appends: 256 per KV head after a 4096-token first write
+
+
+def prefill_leg(reps=5, cpu=True):
     """One 131072-token sequence x 8 KV heads: the multi-token write (rotation on the matrix cores,
-    clip, INT2, pack), then 1024 sequential single-token appends each evicting one window token."""
+    clip, INT2, pack), then 1024 sequential single-token appends each evicting one window token.
+    Returns (report, CPU-oracle legs or {})."""
     import numpy as np
     import torch
 
@@ -251,14 +329,41 @@ def prefill_leg(reps=5):
         f"({res['pct_peak_kernel']}% of 8 TB/s); rotation {res['rotation_tflops_algorithmic']} TFLOP/s algorithmic; "
         f"evict+append step {res['append_step_us']} us")
     del kbuf, vbuf, st
-    return res
+    if not cpu:
+        return res, {}
+    rot1 = [rots[h:h + 1] for h in range(hkv)]
+
+    def write_rep(times, outs, P):
+        par = min(P, hkv)
+        t = float(np.sum(times)) / par
+        return {"value": nbytes / t / 1e9, "unit": "GB/s", "workload": res["workload"].split(", then")[0],
+                "sample": f"all {hkv} KV heads (one job each; inputs drawn untimed) on {par} cores",
+                "seconds_sampled": round(float(np.sum(times)), 3), "seconds_on_P_cores": round(t, 3),
+                "gpu_kernel_over_cpu": round(t * 1e6 / kernel_us, 1)}
+
+    L0, n_app = CPU_APPEND_SAMPLE
+
+    def append_rep(times, outs, P):
+        par = min(P, hkv)
+        per_step = float(np.sum(times)) / n_app / par
+        return {"value": round(per_step * 1e6, 1), "unit": "us per evict+append step (8 KV heads)",
+                "workload": f"{PREFILL_APPENDS} single-token appends each evicting one window token, 8 KV heads",
+                "sample": f"{n_app} appends per KV head after an untimed {L0}-token first write (the oracle's "
+                          f"append cost does not depend on the length), one job per head on {par} cores",
+                "seconds_sampled": round(float(np.sum(times)), 3),
+                "gpu_step_over_cpu": round(per_step * 1e6 / append_us, 1)}
+
+    legs = {"c4_prefill_write": ([("write", cfg, 0, 0, h, L, rot1[h]) for h in range(hkv)], write_rep),
+            "c4_appends": ([("appends", cfg, 0, 0, h, L0, n_app, rot1[h]) for h in range(hkv)], append_rep)}
+    return res, legs
 
 
-def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0, flush_mode="read"):
+def layer_leg(cfg, hq, hkv, lengths, reps, label, cpu_units=None):
     """One attention layer over sequences of the given lengths (one R_K per KV head, pages in a
     seeded shuffled order): prefill writes, then `reps` decode steps (the decode-step write of
     one token per sequence, then decode attention), each after one untimed step.  Returns the
-    split kernel's mean launch time (library events), the whole step's time and their rates."""
+    split kernel's mean launch time (library events), the whole step's time and their rates, and
+    with cpu_units ((seq, KV head) list) the CPU-oracle decode leg on the final state (or None)."""
     import numpy as np
     import torch
 
@@ -273,7 +378,6 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0, flush_mode="read"):
     num_pages = sum(-(-(L + reps + 2) // 64) for L in lengths) + B
     st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, 0, num_pages))
     st.set_rotation(rots)
-    st.set_decode_split(pps)
     prm = sgpu.HeadParams(cfg, 0, hkv)
     n_new = reps + 1
     kbuf = torch.empty((1, max(lengths) + n_new, hkv, 128), dtype=torch.int16, device="cuda")
@@ -309,10 +413,7 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0, flush_mode="read"):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     flush.fill_(1)
     for i in range(reps):
-        if flush_mode == "write":
-            flush.fill_(i)
-        else:
-            flush.sum()
+        flush.sum()
         evs[i][0].record()
         step(1 + i)
         evs[i][1].record()
@@ -336,8 +437,13 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, pps=0, flush_mode="read"):
     }
     log(f"{label}: split kernel {res['split_kernel_us']} us = {res['split_kernel_gbps']} GB/s "
         f"({res['split_kernel_pct_peak']}% of 8 TB/s); step (write + attention) {res['step_us_median']} us")
+    leg = None
+    if cpu_units:
+        st.decode(seqs, q, scale, out=out, ws=ws)
+        torch.cuda.synchronize()
+        leg = decode_leg(st, cpu_units, rots, q.cpu().numpy().view(np.uint16), out.cpu().numpy(), hq, hkv, label)
     del st, newk, newv, ws, flush
-    return res
+    return res, leg
 
 
 def main():
@@ -345,30 +451,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=36, help="development only: fewer layers")
-    ap.add_argument("--context", type=int, default=100000, help="development only")
-    ap.add_argument("--batch", type=int, default=32, help="development only")
+    ap.add_argument("--layers", type=int, default=36,
+                    help="layers of the step (36; fewer only for short profiled runs, reported as such)")
     ap.add_argument("--attn-reps", type=int, default=3)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
-                    help="run a plain device copy of this size at the end (counter scaling in profiled runs)")
-    ap.add_argument("--cpu-units", type=int, default=32)
+                    help="run a plain device copy of this size at the end (scales the memory counters of a "
+                         "profiled run)")
+    ap.add_argument("--cpu-units", type=int, default=16, help="sampled (seq, kv head) units of the CPU-oracle decode leg of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the 131072-token prefill-write leg")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the single-layer legs (32K x 8 GQA 4; ragged 8K-128K x 16 GQA 8)")
-    ap.add_argument("--pps", type=int, default=0, help="pages per decode split (0 = library choice)")
-    ap.add_argument("--sweep-pps", default="", help="development: comma list of split sizes to time")
-    ap.add_argument("--deterministic", action="store_true",
-                    help="fixed page range per split (no page sharing between the splits of a unit)")
-    ap.add_argument("--kernel", type=int, default=0, help="decode kernel: 0 matrix-core, 1 reference")
-    ap.add_argument("--layer-pps", type=int, default=0,
-                    help="development: pages per decode split in the single-layer legs (0 = library choice)")
-    ap.add_argument("--layer-flush", choices=["write", "read"], default="read",
-                    help="development: how the single-layer legs push their cache out of the last-level cache")
-    ap.add_argument("--two-call", action="store_true",
-                    help="development: the decode-step write and the attention as two calls")
-    ap.add_argument("--separate-write", action="store_true",
-                    help="write each step with the eviction and the append as two calls (comparison)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -386,7 +479,7 @@ def main():
     oscar.load()
     torch.cuda.set_device(0)
     cfg = synth.CFG_QWEN3_8B
-    n_layers, B, ctx = args.layers, args.batch, args.context
+    n_layers, B, ctx = args.layers, 32, 100000
     hq, hkv = 32, 8
     # warmup, the timed steps, then warmup and the kernel-timed steps again
     n_steps_total = 2 * args.warmup + 2 * args.steps
@@ -415,9 +508,6 @@ def main():
     for l in range(n_layers):
         st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, l, num_pages))
         st.set_rotation(rots[l])
-        st.set_decode_split(args.pps)
-        st.set_decode_kernel(args.kernel)
-        st.set_decode_deterministic(args.deterministic)
         prm = sgpu.HeadParams(cfg, l, hkv)
         for s in range(B):
             sgpu.draw_kv(prm, s, 0, ctx, kbuf[0], vbuf[0])
@@ -448,22 +538,15 @@ def main():
     # layer-0 decode on the prefill state, kept for the CPU-oracle sample check
     stores[0].decode(seqs, qs[0], scale, out=outs[0], ws=ws)
     torch.cuda.synchronize()
-    out_layer0 = outs[0].cpu().numpy()
-    q_layer0 = qs[0].cpu().numpy().view(np.uint16)
-    units0 = [] if args.no_cpu_baseline else export_units(stores[0], CPU_UNITS[:args.cpu_units])
+    legs = {}
+    if not args.no_cpu_baseline:
+        legs["c2_decode"] = decode_leg(stores[0], CPU_UNITS[:args.cpu_units], rots[0],
+                                       qs[0].cpu().numpy().view(np.uint16), outs[0].cpu().numpy(), hq, hkv,
+                                       "decode attention of the step (all layers) on the prefill state", n_layers)
 
     def step(i):
         for l in range(n_layers):
-            st = stores[l]
-            if args.separate_write:
-                st.evict(seqs, 1)
-                st.write(seqs, newk[l, i], newv[l, i])
-                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
-            elif args.two_call:
-                st.decode_write(seqs, newk[l, i, :, 0], newv[l, i, :, 0])
-                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
-            else:
-                st.decode_step(seqs, newk[l, i, :, 0], newv[l, i, :, 0], qs[l], scale, out=outs[l], ws=ws)
+            stores[l].decode_step(seqs, newk[l, i, :, 0], newv[l, i, :, 0], qs[l], scale, out=outs[l], ws=ws)
 
     def step_bytes():
         tot = 0
@@ -535,51 +618,56 @@ def main():
         f"{kernel_gbps:.0f} GB/s ({100 * kernel_gbps / PEAK_GBPS:.1f}% of 8 TB/s); "
         f"those steps took {ms_per_step_kt:.2f} ms each")
 
-    # ---- development sweep of the split size (attention only)
-    for pps in [int(x) for x in args.sweep_pps.split(",") if x]:
-        for st in stores:
-            st.set_decode_split(pps)
-        need = max(st.workspace_bytes(seqs) for st in stores)
-        if need > ws.numel() * 4:
-            ws = torch.empty(need // 4 + 1, dtype=torch.float32, device="cuda")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for st in stores:
-            st.decode(seqs, qs[0], scale, out=outs[0], ws=ws)
-            st.set_timing(True)
-        e0.record()
-        for r in range(2):
-            for l, st in enumerate(stores):
-                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (2 * n_layers)
-        k_n, k_ms = 0, 0.0
-        for st in stores:
-            n, ms = st.read_timing(oscar.TIMED_DECODE)
-            k_n, k_ms = k_n + n, k_ms + ms
-            st.set_timing(False)
-        log(f"sweep pps={pps}: split kernel {k_ms * 1e3 / max(k_n, 1):.1f} us, call {us:.1f} us/layer")
-    for st in stores:
-        st.set_decode_split(args.pps)
-
-    # ---- attention-only pass over the frozen cache: per-call HIP events on the launch stream
-    per_call = []
+    # ---- attention-only passes over the frozen cache, default mode (a unit's INT2 splits share
+    # page groups at run time) and deterministic mode (fixed page range per split): per-call HIP
+    # events on the launch stream, and the library's events around each split-kernel launch
     attn_bytes = []
     for st in stores:
         info = [st.seq_info(s) for s in seqs]
         attn_bytes.append(decode_bytes([L for L, _ in info], [n2 for _, n2 in info], hq, hkv))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
-    for r in range(args.attn_reps):
-        for l, st in enumerate(stores):
-            evs[l][0].record()
-            st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
-            evs[l][1].record()
-        torch.cuda.synchronize()
-        per_call.extend(a.elapsed_time(b) for a, b in evs)
-    attn_ms = float(np.mean(per_call))
-    attn_gbps = float(np.mean(attn_bytes)) / (attn_ms / 1e3) / 1e9
-    log(f"attention-only: {attn_ms * 1e3:.1f} us/layer, {attn_gbps:.0f} GB/s ({100 * attn_gbps / PEAK_GBPS:.1f}% of 8 TB/s)")
 
+    def attn_pass(deterministic):
+        per_call, repeat = [], None
+        for st in stores:
+            st.set_decode_deterministic(deterministic)
+            st.set_timing(True)
+        for r in range(args.attn_reps + 1):
+            for l, st in enumerate(stores):
+                evs[l][0].record()
+                st.decode(seqs, qs[l], scale, out=outs[l], ws=ws)
+                evs[l][1].record()
+            torch.cuda.synchronize()
+            if r == 0:                       # untimed pass; keep layer 0's output
+                first = outs[0].clone()
+                for st in stores:
+                    st.read_timing(oscar.TIMED_DECODE)
+                continue
+            per_call.extend(a.elapsed_time(b) for a, b in evs)
+            repeat = bool(torch.equal(first, outs[0]))
+        n_k, ms_k = 0, 0.0
+        for st in stores:
+            n, ms = st.read_timing(oscar.TIMED_DECODE)
+            n_k += n
+            ms_k += ms
+            st.set_timing(False)
+            st.set_decode_deterministic(False)
+        call_ms = float(np.mean(per_call))
+        gbps = float(np.mean(attn_bytes)) / (call_ms / 1e3) / 1e9
+        return {"us_per_layer": round(call_ms * 1e3, 2), "gbps": round(gbps, 1),
+                "pct_peak": round(100 * gbps / PEAK_GBPS, 2), "bytes_per_layer": int(np.mean(attn_bytes)),
+                "split_kernel_us": round(ms_k * 1e3 / n_k, 2),
+                "split_kernel_pct_peak": round(100 * kernel_bytes / (ms_k * 1e3 / n_k) / 1e3 / PEAK_GBPS, 2),
+                "layer0_output_bitwise_repeats": repeat}
+
+    attn = attn_pass(False)
+    attn_det = attn_pass(True)
+    for name, a in (("attention-only", attn), ("attention-only, deterministic", attn_det)):
+        log(f"{name}: {a['us_per_layer']} us/layer, {a['gbps']} GB/s ({a['pct_peak']}% of 8 TB/s); split kernel "
+            f"{a['split_kernel_us']} us ({a['split_kernel_pct_peak']}%); layer-0 output repeats bitwise: "
+            f"{a['layer0_output_bitwise_repeats']}")
+    if not attn_det["layer0_output_bitwise_repeats"]:
+        raise RuntimeError("deterministic decode did not repeat bitwise")
     result = {
         "metric": METRIC,
         "value": round(step_gbps, 1),
@@ -593,7 +681,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "int2 KV (fp16 scale/min per 64) + bf16 ring; Q.K on i8 MFMA with q' as two int8 terms, "
+                 "P.V on f16 MFMA with P as an f16 hi+lo pair; f32 accumulate, f32 output",
         "data": "synthetic (seeded; keys/values drawn on the GPU, Philox4x32-10)",
         "config": {
             "workload": (f"qwen3-8b-shaped decode step: {n_layers} layers x (write: evict 1 + append 1, "
@@ -601,13 +690,10 @@ def main():
                          "INT2 KV in 64-token pages (shuffled), BF16 sink 64 + window 256"),
             "layers": n_layers, "batch": B, "context": ctx, "q_heads": hq, "kv_heads": hkv,
             "headline_config": full,
-            "write_calls": ("evict + append, then attention" if args.separate_write else
-                            "decode-step write, then attention" if args.two_call else
-                            "one decode-step call (write + attention)"),
+            "write_calls": "one decode-step call per layer (write + attention)",
         },
-        "attn_only": {"us_per_layer": round(attn_ms * 1e3, 2), "gbps": round(attn_gbps, 1),
-                      "pct_peak": round(100 * attn_gbps / PEAK_GBPS, 2),
-                      "bytes_per_layer": int(np.mean(attn_bytes))},
+        "attn_only": attn,
+        "attn_only_deterministic": attn_det,
         "roofline": {
             "bound": "hbm",
             "achieved": round(kernel_gbps, 1),
@@ -628,17 +714,20 @@ def main():
                     "p90": round(float(np.percentile(step_ms, 90)), 4),
                     "mean_with_kernel_events": round(ms_per_step_kt, 4)},
     }
+    cpu = not args.no_cpu_baseline
     if not args.no_prefill:
-        result["prefill"] = prefill_leg()
+        result["prefill"], pl = prefill_leg(cpu=cpu)
+        legs.update(pl)
     if not args.no_layers:
-        result["layer_qwen3_4b_32k_b8"] = layer_leg(
+        c1_units = [(s, (3 * s + 1) % 8) for s in range(8)] + [(s, (3 * s + 5) % 8) for s in range(8)]
+        result["layer_qwen3_4b_32k_b8"], legs["c1_decode"] = layer_leg(
             synth.CFG_QWEN3_4B, 32, 8, [32768] * 8, 20,
-            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context", pps=args.layer_pps,
-            flush_mode=args.layer_flush)
-        result["layer_qwen3_32b_ragged_b16"] = layer_leg(
+            "qwen3-4b-shaped layer: 32 q / 8 kv heads, batch 8, 32768-token context",
+            c1_units if cpu else None)
+        result["layer_qwen3_32b_ragged_b16"], legs["c3_decode"] = layer_leg(
             synth.CFG_QWEN3_32B, 64, 8, [int(x) for x in synth.ragged_lengths(synth.CFG_QWEN3_32B, 16, 8192, 131072)],
             20, "qwen3-32b-shaped layer: 64 q / 8 kv heads (GQA 8), batch 16, lengths U[8192, 131072]",
-            pps=args.layer_pps, flush_mode=args.layer_flush)
+            [(s, (5 * s + 2) % 8) for s in range(16)] if cpu else None)
     if args.copy_calib_mib:
         # a plain copy of known size, for scaling the memory counters of a profiled run
         n = args.copy_calib_mib * (1 << 20) // 4
@@ -648,11 +737,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy calibration: {args.copy_calib_mib} MiB read + {args.copy_calib_mib} MiB written")
-    if not args.no_cpu_baseline:
-        total_units = n_layers * B * hkv
-        step_attn_bytes = float(np.sum(attn_bytes))
-        result["cpu_baseline"] = cpu_baseline(units0, rots, q_layer0, out_layer0, hq, hkv, total_units,
-                                              step_attn_bytes)
+    if cpu:
+        result["cpu_baseline"] = cpu_baseline({k: v for k, v in legs.items() if v is not None})
     print(json.dumps(result), flush=True)
 
 

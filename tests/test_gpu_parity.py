@@ -377,6 +377,80 @@ def test_keys_outside_fp16_range(gpu_lib):
     assert np.all(np.isfinite(out)) and parity.rel_l2(out, iso) <= ISO_TOL
 
 
+def test_sequence_reset_and_page_reuse(gpu_lib):
+    """A sequence is reset and a new one is written into its recycled pages, which still hold the
+    old codes: the device page-table row is cleared, the FIFO and page tables follow the oracle
+    exactly, the new prefill's INT2 pages and ring match the oracle under the tolerance rules,
+    and decode steps whose eviction takes a recycled page (zeroed on its first token) stay
+    bit-exact on the evicted tokens and within the decode bounds."""
+    import torch
+    hkv, hq = 2, 8
+    _case("sequence reset and page reuse")
+    rot = parity.calibrate(synth.CFG_QWEN3_4B, 11, hkv)
+    # pages: seq 0 four, seq 1 three, seq 2 three, one spare -> after the reset of seq 1 the FIFO
+    # holds the spare, then seq 1's pages in ascending logical order
+    lengths = {0: 320 + 64 * 3 + 10, 1: 320 + 64 * 2 + 40, 2: 500}
+    n_pages = 11
+    free = synth.page_permutation(synth.CFG_QWEN3_4B, 11, n_pages)
+    st = _store(gpu_lib, hq, hkv, 3, 8, n_pages, free, rot)
+    ora = ostore.OracleStore(hkv, 3, 8, n_pages, free, rot)
+    ks, vs = _kv_batch(synth.CFG_QWEN3_4B, [0, 1, 2], hkv, 600)
+    inputs = {}
+    for s_, L in lengths.items():
+        st.write([s_], parity.to_dev_bf16(ks[s_:s_ + 1, :L]), parity.to_dev_bf16(vs[s_:s_ + 1, :L]))
+        ora.write([s_], ks[s_:s_ + 1, :L], vs[s_:s_ + 1, :L])
+        inputs[s_] = (ks[s_, :L], vs[s_, :L], L)
+    old_pages = [int(p) for p in ora.page_table[1, :3]]
+    st.reset_seq(1)
+    ora.reset_seq(1)
+    torch.cuda.synchronize()
+    assert st.seq_info(1) == (0, 0)
+    assert (st.table_view().cpu().numpy()[1] == -1).all()
+    assert list(st.free_pages()) == list(ora.free) and list(ora.free)[1:] == old_pages
+    # the new sequence 1: different tokens, 3 INT2 pages (the spare and two recycled ones), a
+    # full window, so its first eviction (INT2 index 192) takes the last recycled page
+    kn, vn = _kv_batch(synth.CFG_QWEN3_4B, [7], hkv, 512 + 12, token0=1000)
+    st.write([1], parity.to_dev_bf16(kn[:, :512]), parity.to_dev_bf16(vn[:, :512]))
+    ora.write([1], kn[:, :512], vn[:, :512])
+    inputs[1] = (kn[0, :512], vn[0, :512], 512)
+    gpu = parity.export(st)
+    assert np.array_equal(gpu[2], ora.page_table) and set(ora.page_table[1, :3]) <= set(old_pages + [int(free[-1])])
+    _check_state(gpu, ora, [0, 1, 2], rot, inputs)
+    ids = [1, 0, 2]
+    pos = {0: lengths[0], 1: 512, 2: lengths[2]}
+    src = {0: (ks, 0), 1: (kn, 0), 2: (ks, 2)}
+    vsrc = {0: vs, 1: vn, 2: vs}
+    for step in range(12):
+        kt = np.stack([src[s_][0][src[s_][1], pos[s_]] for s_ in ids])
+        vt = np.stack([vsrc[s_][src[s_][1], pos[s_]] for s_ in ids])
+        q = synth.decode_queries(synth.CFG_QWEN3_4B, 11, 3, hq, hkv, step=step)
+        ring_before = parity.export(st)[1]
+        n2_before = {s_: int(ora.n_int2[s_]) for s_ in ids}
+        full = [s_ for s_ in ids if int(ora.length[s_]) - 64 - int(ora.n_int2[s_]) == 256]
+        out = st.decode_step(ids, parity.to_dev_bf16(kt), parity.to_dev_bf16(vt), parity.to_dev_bf16(q), SCALE)
+        if full:
+            ora.evict(full, 1)
+        ora.write(ids, kt[:, None], vt[:, None])
+        for s_ in ids:
+            pos[s_] += 1
+        gpu = parity.export(st)
+        assert np.array_equal(gpu[2], ora.page_table), step
+        assert list(st.free_pages()) == list(ora.free), step
+        for s_ in full:
+            parity.check_evicted(gpu[0], gpu[2], ring_before, s_, n2_before[s_])
+        iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, ids, SCALE, hq)
+        assert parity.rel_l2(out.cpu().numpy(), iso) <= ISO_TOL, step
+    # the new sequence's first eviction took the last recycled page, whose other slots are zero
+    assert int(ora.n_int2[1]) == 192 + 12 and int(ora.page_table[1, 3]) in old_pages
+    blk = gpu[0][int(ora.page_table[1, 3]), :]
+    from oracle import layout
+    for h in range(hkv):
+        unpacked = layout.unpack_head_block(blk[h])
+        assert all(not np.ascontiguousarray(a_[12:]).view(np.uint8).any() for a_ in unpacked), h
+    ref = attention.decode_store(ora, q, ids, SCALE, hq)
+    _e2e(out.cpu().numpy(), ref)
+
+
 def test_more_sequences_than_one_launch(gpu_lib):
     """70 sequences (a launch takes at most 64): one batched first write, then three one-call decode
     steps (each evicting, pages crossing at INT2 index 128) and an attention call, all with the
