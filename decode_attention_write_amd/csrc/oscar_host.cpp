@@ -76,46 +76,19 @@ constexpr int64_t kPage = OSCAR_PAGE_TOKENS;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// IEEE binary16 from/to binary32 on the host, round to nearest even (normals, subnormals, zero;
-// the inputs here are finite and far below the fp16 limit).
-uint16_t f32_to_f16_rn(float x) {
+// bfloat16 from/to binary32 on the host: round to nearest even (finite inputs), and exact widening.
+uint16_t f32_to_bf16_rn(float x) {
   uint32_t u;
   std::memcpy(&u, &x, 4);
-  const uint32_t sign = (u >> 16) & 0x8000u;
-  const uint32_t ax = u & 0x7FFFFFFFu;
-  if (ax >= 0x477FF000u) return static_cast<uint16_t>(sign | 0x7C00u);   // rounds to >= 65520: inf
-  if (ax < 0x38800000u) {                                                // below 2^-14: subnormal
-    // value = ax_float; subnormal step 2^-24: q = round_half_even(x * 2^24)
-    float a;
-    const uint32_t axu = ax;
-    std::memcpy(&a, &axu, 4);
-    const float q = std::nearbyint(a * 16777216.0f);                      // exact scaling; RNE mode
-    return static_cast<uint16_t>(sign | static_cast<uint32_t>(q));
-  }
-  // normal: keep 10 mantissa bits, round to nearest even on the 13 dropped bits
-  const uint32_t exp16 = ((ax >> 23) - 112u) << 10;
-  const uint32_t mant = ax & 0x7FFFFFu;
-  uint32_t h = exp16 | (mant >> 13);
-  const uint32_t rem = mant & 0x1FFFu;
-  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;             // may carry into the exponent
-  return static_cast<uint16_t>(sign | h);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
 }
 
-float f16_to_f32(uint16_t h) {
-  const uint32_t sign = static_cast<uint32_t>(h & 0x8000u) << 16;
-  const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
-  float v;
-  if (e == 0) {
-    v = std::ldexp(static_cast<float>(m), -24);
-  } else {
-    const uint32_t u = ((e + 112u) << 23) | (m << 13);
-    std::memcpy(&v, &u, 4);
-  }
-  uint32_t u;
-  std::memcpy(&u, &v, 4);
-  u |= sign;
-  std::memcpy(&v, &u, 4);
-  return v;
+float bf16_to_f32(uint16_t b) {
+  const uint32_t u = static_cast<uint32_t>(b) << 16;
+  float x;
+  std::memcpy(&x, &u, 4);
+  return x;
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -494,9 +467,9 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
   for (size_t i = 0; i < n; ++i)
     if (!std::isfinite(rot_host[i])) { set_error("oscar_kv_set_rotation: non-finite entry"); return OSCAR_E_NUMERIC; }
   if (kv->plan_only) { kv->has_rotation = true; return OSCAR_OK; }
-  // per head: fp32 R, then two fp16 terms r0 + r1 ~= 2^14 R (r0 = fp16(2^14 R), r1 = fp16(2^14 R - r0),
-  // |2^14 R - r0 - r1| <= 2^-22 |2^14 R|), stored transposed ([term][output channel c][input
-  // channel i]) for the write kernel's MFMA A operand; a third 32 KB slot is left zero
+  // per head: fp32 R, then three bf16 terms r0 + r1 + r2 ~= R (r0 = bf16(R), r1 = bf16(R - r0),
+  // r2 = bf16(R - r0 - r1); the fp32 differences are exact, |R - r0 - r1 - r2| <= 2^-24 |R|), stored
+  // transposed ([term][output channel c][input channel i]) for the write kernel's MFMA A operand
   std::vector<uint8_t> blob(static_cast<size_t>(hkv) * OSCAR_ROT_HEAD_BYTES, 0);
   const size_t dd = OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
   for (int h = 0; h < hkv; ++h) {
@@ -505,11 +478,14 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
     uint16_t* terms = reinterpret_cast<uint16_t*>(base + dd * 4);
     for (size_t i = 0; i < OSCAR_HEAD_DIM; ++i)
       for (size_t c = 0; c < OSCAR_HEAD_DIM; ++c) {
-        const float scaled = rot_host[h * dd + i * OSCAR_HEAD_DIM + c] * 16384.0f;   // exact
-        const uint16_t t0 = f32_to_f16_rn(scaled);
-        const uint16_t t1 = f32_to_f16_rn(scaled - f16_to_f32(t0));              // exact difference
+        const float r = rot_host[h * dd + i * OSCAR_HEAD_DIM + c];
+        const uint16_t t0 = f32_to_bf16_rn(r);
+        const float d1 = r - bf16_to_f32(t0);
+        const uint16_t t1 = f32_to_bf16_rn(d1);
+        const uint16_t t2 = f32_to_bf16_rn(d1 - bf16_to_f32(t1));
         terms[c * OSCAR_HEAD_DIM + i] = t0;
         terms[dd + c * OSCAR_HEAD_DIM + i] = t1;
+        terms[2 * dd + c * OSCAR_HEAD_DIM + i] = t2;
       }
   }
   hipError_t e = hipMemcpyAsync(kv->desc.rot, blob.data(), blob.size(), hipMemcpyHostToDevice, as_stream(stream));

@@ -120,9 +120,9 @@ typedef struct oscar_kv oscar_kv;
  *             lives in page page_table[seq][i / 64], slot i % 64.
  * rot         device, num_kv_heads * OSCAR_ROT_HEAD_BYTES bytes, written by
  *             oscar_kv_set_rotation: per KV head R_K fp32 [128][128] followed by
- *             two fp16 [128][128] terms of 2^14 R_K^T (term t, output channel c,
- *             input channel i; r0 = fp16(2^14 R^T), r1 = fp16(2^14 R^T - r0), whose
- *             sum is 2^14 R^T within 2^-22 of it) and a 32 KB slot left zero.
+ *             three bf16 [128][128] terms of R_K^T (term t, output channel c,
+ *             input channel i; r0 = bf16(R^T), r1 = bf16(R^T - r0),
+ *             r2 = bf16(R^T - r0 - r1), whose sum is R^T within 2^-24 of it).
  */
 typedef struct {
     int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads with Hq/Hkv <= 8 */

@@ -58,17 +58,15 @@ def fp16_ulp_diff(a, b):
 
 def rotation_error_bound(k_bits, rot_h):
     """Per-element bound on |x_gpu - k.R| for keys rotated on the matrix cores (bf16 [n, 128] keys,
-    one head's fp32 R).  The write kernel carries S R^T (S = 2^14) as two fp16 terms r0 =
-    fp16(S R^T), r1 = fp16(S R^T - r0), so |S R - r0 - r1| <= 2^-22 |S R| + 2^-25 (fp16 unit
-    roundoff 2^-11 twice; the last term is the fp16 denormal grid); each key row is scaled by a
-    power of two into [2^14, 2^15) before an fp16 conversion that is exact down to 2^-24 of the
-    row's largest entry (2^-39 of it below that); the products are exact in fp32 and the 256 of
-    them go through 8 matrix instructions of 32 into an fp32 accumulator: up to 32 roundings of at
-    most sum_i |k_i R_ij| each are allowed (2^-19).  Returns [n, 128]."""
+    one head's fp32 R).  The write kernel carries R^T as three bf16 terms r0 = bf16(R^T), r1 =
+    bf16(R^T - r0), r2 = bf16(R^T - r0 - r1), so |R - r0 - r1 - r2| <= 2^-24 |R| (bf16 unit
+    roundoff 2^-8, three times); the bf16 keys enter as they are; the products are exact in fp32
+    and the 384 of them go through 12 matrix instructions of 32 into an fp32 accumulator: up to 48
+    roundings of at most (1 + 2^-7) sum_i |k_i R_ij| each are allowed.  Products or inputs below
+    the fp32 normal range may be flushed: 2^-116 absolute covers 384 of them.  Returns [n, 128]."""
     k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
     r = np.asarray(rot_h, np.float32).astype(np.float64)
-    kmax = np.abs(k).max(axis=1, keepdims=True)
-    return (np.abs(k) @ np.abs(r)) * (2.0 ** -22 + 2.0 ** -19) + 2.0 ** -30 * kmax
+    return (np.abs(k) @ np.abs(r)) * (2.0 ** -24 + 48 * (1 + 2.0 ** -7) * 2.0 ** -24) + 2.0 ** -116
 
 
 def _ulp32(x):
@@ -224,17 +222,16 @@ def check_evicted(pool, table, ring_before, seq, n2, heads=None):
 
 def ring_key_bound(k_bits, rot_h):
     """Allowed |stored bf16 key - exact k.R| per channel, besides half a bf16 ulp of the stored value.
-    Multi-token writes rotate on the matrix cores (rotation_error_bound: fp16 terms of 2^14 R^T
-    within 2^-22 of it, exact products, fp32 accumulation); single-token appends use a 128-term
-    fp32 dot product.  Both stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-22 sum_i
-    |k_i R_ij| + 2^-30 max|k| (dot-product forward-error bound, Higham, Accuracy and Stability of
-    Numerical Algorithms, section 3.1).  Returns (bound, exact k.R) [n, 128]."""
+    Multi-token writes rotate on the matrix cores (rotation_error_bound: bf16 terms of R^T within
+    2^-24 of it, exact products, fp32 accumulation); single-token appends use a 128-term fp32 dot
+    product.  Both stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-24 sum_i |k_i R_ij| +
+    2^-116 (dot-product forward-error bound, Higham, Accuracy and Stability of Numerical
+    Algorithms, section 3.1).  Returns (bound, exact k.R) [n, 128]."""
     k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
     r = np.asarray(rot_h, np.float32).astype(np.float64)
     u = 2.0 ** -24
     gamma = 256 * u / (1 - 256 * u)
-    kmax = np.abs(k).max(axis=1, keepdims=True)
-    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -22) + 2.0 ** -30 * kmax, k @ r
+    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -24) + 2.0 ** -116, k @ r
 
 
 def bf16_ulp(x):

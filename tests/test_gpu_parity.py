@@ -132,8 +132,8 @@ def test_generator_gpu_twin_bit_exact(gpu_lib):
 
 
 def test_rotation_blob_terms(gpu_lib):
-    """The device rotation block of each KV head: fp32 R, then fp16 r0 = fp16(2^14 R^T) and
-    r1 = fp16(2^14 R^T - r0) (round to nearest even; numpy's conversions), then a zero slot."""
+    """The device rotation block of each KV head: fp32 R, then the bf16 terms r0 = bf16(R^T),
+    r1 = bf16(R^T - r0), r2 = bf16(R^T - r0 - r1) (round to nearest even)."""
     _case("rotation blob")
     rot = parity.calibrate(synth.CFG_QWEN3_4B, 3, 2)
     st = _store(gpu_lib, 8, 2, 1, 4, 4, None, rot)
@@ -142,12 +142,13 @@ def test_rotation_blob_terms(gpu_lib):
     blob = st.rot.cpu().numpy().reshape(2, -1)
     for h in range(2):
         assert np.array_equal(blob[h, :65536].view(np.float32).reshape(128, 128), rot[h])
-        rs = rot[h].T.astype(np.float32) * np.float32(16384)
-        r0 = rs.astype(np.float16)
-        r1 = (rs - r0.astype(np.float32)).astype(np.float16)
+        rt = np.ascontiguousarray(rot[h].T.astype(np.float32))
+        t0 = synth.f32_to_bf16_bits(rt)
+        d1 = rt - synth.bf16_bits_to_f32(t0)
+        t1 = synth.f32_to_bf16_bits(d1)
+        t2 = synth.f32_to_bf16_bits(d1 - synth.bf16_bits_to_f32(t1))
         terms = blob[h, 65536:].view(np.uint16).reshape(3, 128, 128)
-        assert np.array_equal(terms[0], r0.view(np.uint16)) and np.array_equal(terms[1], r1.view(np.uint16))
-        assert not terms[2].any()
+        assert np.array_equal(terms[0], t0) and np.array_equal(terms[1], t1) and np.array_equal(terms[2], t2)
 
 
 def test_tiny_config_write_and_decode(gpu_lib):
@@ -344,13 +345,13 @@ def test_degenerate_and_extreme_groups(gpu_lib):
 
 
 def test_keys_outside_fp16_range(gpu_lib):
-    """Keys that fp16 does not represent exactly (entries >= 2^16, rows of values below 2^-14, rows
-    mixing both scales) make the write kernel scale each key row by a power of two before its
-    fp16 rotation: stored state under the tolerance rules (key-metadata flips explained by the
-    rotation error) with a calibrated rotation, and decode parity on identical state."""
+    """Keys of extreme magnitudes (entries >= 2^16, rows of values below 2^-14, rows mixing both
+    scales), which the matrix-core rotation takes as they are: stored state under the tolerance
+    rules (key-metadata flips explained by the rotation error) with a calibrated rotation, and
+    decode parity on identical state."""
     hkv, hq = 2, 8
     L = 320 + 64 * 3 + 5
-    _case("keys outside the fp16 range (scaled rotation path)")
+    _case("keys of extreme magnitudes")
     rot = parity.calibrate(synth.CFG_QWEN3_4B, 10, hkv)
     rng = np.random.default_rng(17)
     k = rng.standard_normal((L, hkv, D)).astype(np.float32)

@@ -19,28 +19,20 @@ def _bf16_round(x):
     return u.astype(np.uint32).view(np.float32)
 
 
-def _f16_round(x):
-    return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
-
-
 def _emulated_rotation(k, r):
-    """k . R as the write kernel forms it: 2^14 R as two fp16 terms, each key row scaled by the
-    power of two that puts its largest magnitude in [2^14, 2^15) and converted to fp16, exact
-    products, each of the 8 partial sums (4 K-steps of 32 channels x 2 terms) rounded once into
-    an fp32 accumulator, then unscaled."""
-    rs = r.astype(np.float64) * 2.0 ** 14
-    r0 = _f16_round(rs)
-    r1 = _f16_round(rs - r0)
-    mx = np.abs(k).max(axis=1, keepdims=True)
-    ex = np.floor(np.log2(np.where(mx > 0, mx, 1.0)))
-    sc = np.ldexp(1.0, (14 - ex).astype(int))
-    ks = _f16_round(k * sc).astype(np.float64)
+    """k . R as the write kernel forms it: R as three bf16 terms, the bf16 keys as they are, exact
+    products, each of the 12 partial sums (3 terms x 4 K-steps of 32 channels, the smallest term
+    first) rounded once into an fp32 accumulator."""
+    t0 = _bf16_round(r)
+    d1 = (r - t0).astype(np.float32)
+    t1 = _bf16_round(d1)
+    t2 = _bf16_round((d1 - t1).astype(np.float32))
     acc = np.zeros((k.shape[0], D), np.float32)
-    for kk in range(4):
-        sl = slice(32 * kk, 32 * kk + 32)
-        for rr in (r1, r0):
-            acc = (acc.astype(np.float64) + ks[:, sl] @ rr[sl].astype(np.float64)).astype(np.float32)
-    return (acc.astype(np.float64) / sc / 2.0 ** 14).astype(np.float32)
+    for rr in (t2, t1, t0):
+        for kk in range(4):
+            sl = slice(32 * kk, 32 * kk + 32)
+            acc = (acc.astype(np.float64) + k[:, sl] @ rr[sl].astype(np.float64)).astype(np.float32)
+    return acc
 
 
 def _setup(n=40000):
@@ -57,14 +49,14 @@ def test_rotation_error_bound_holds_for_emulated_kernel():
     k, r, x_ref, bound = _setup()
     x_gpu = _emulated_rotation(k, r).astype(np.float64)
     assert np.all(np.abs(x_gpu - x_ref) <= bound)
-    # the fp16 split of 2^14 R: residual within 2^-22 |2^14 R| + 2^-25 (fp16 denormal grid)
-    rs = r.astype(np.float64) * 2.0 ** 14
-    r0 = _f16_round(rs)
-    res = np.abs(rs - r0 - _f16_round(rs - r0))
-    assert np.all(res <= 2.0 ** -22 * np.abs(rs) + 2.0 ** -25)
-    # a bf16 split (two terms) is 2^6 coarser: its residual exceeds 2^-18 |R|
-    b0 = _bf16_round(r)
-    assert (np.abs(r.astype(np.float64) - b0 - _bf16_round(r - b0)) / np.abs(r)).max() > 2.0 ** -18
+    # the bf16 split of R: residual within 2^-24 |R|; two terms leave a residual above 2^-18 |R|
+    rr = r.astype(np.float64)
+    t0 = _bf16_round(r)
+    d1 = (r - t0).astype(np.float32)
+    t1 = _bf16_round(d1)
+    t2 = _bf16_round((d1 - t1).astype(np.float32))
+    assert np.all(np.abs(rr - t0 - t1 - t2) <= 2.0 ** -24 * np.abs(rr))
+    assert (np.abs(rr - t0 - t1) / np.abs(rr)).max() > 2.0 ** -18
 
 
 def test_key_metadata_flips_explained_only_by_rotation_error():
