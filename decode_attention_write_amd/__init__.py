@@ -43,7 +43,7 @@ EXPORTS = [
     "oscar_kv_set_timing",
     "oscar_kv_read_timing", "oscar_last_error", "oscar_kv_destroy",
     "oscar_decode_step_workspace_bytes", "oscar_decode_step", "oscar_kv_set_write_evicts",
-    "oscar_kv_set_output_bf16", "oscar_decode_step_noalloc",
+    "oscar_kv_set_output_bf16", "oscar_decode_step_noalloc", "oscar_kv_set_key_mean",
 ]
 NOALLOC_SCRATCH_BYTES = 32 << 20   # OSCAR_NOALLOC_SCRATCH_BYTES
 
@@ -81,6 +81,7 @@ def load():
         "oscar_kv_buffer_bytes": [P, P, P, P, P],
         "oscar_kv_create": [P, P, I32, P, P],
         "oscar_kv_set_rotation": [P, P, P],
+        "oscar_kv_set_key_mean": [P, P, P],
         "oscar_kv_write": [P, P, I32, I32, P, P, P],
         "oscar_kv_evict_window": [P, P, I32, I32, P],
         "oscar_decode_workspace_bytes": [P, P, I32, P],
@@ -349,6 +350,16 @@ class KVStore:
     def set_rotation(self, rot, stream=None):
         r = np.ascontiguousarray(np.asarray(rot, dtype=np.float32).reshape(self.hkv, HEAD_DIM, HEAD_DIM))
         _check(load().oscar_kv_set_rotation(self.handle, r.ctypes.data_as(ctypes.c_void_p),
+                                            None if self.plan_only else _stream(stream)))
+
+    def set_key_mean(self, mean, stream=None):
+        """Per-KV-head key mean subtracted from every key written afterwards (fp32 [hkv, 128]),
+        or None to write keys as they are."""
+        if mean is None:
+            _check(load().oscar_kv_set_key_mean(self.handle, None, None if self.plan_only else _stream(stream)))
+            return
+        m = np.ascontiguousarray(np.asarray(mean, dtype=np.float32).reshape(self.hkv, HEAD_DIM))
+        _check(load().oscar_kv_set_key_mean(self.handle, m.ctypes.data_as(ctypes.c_void_p),
                                             None if self.plan_only else _stream(stream)))
 
     def write(self, seq_ids, k, v, stream=None, n_new=None):

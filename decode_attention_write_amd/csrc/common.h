@@ -29,7 +29,9 @@ constexpr int HEAD_BLOCK = 5120;
 constexpr int KC_OFF = 0;
 constexpr int VC_OFF = 2048;
 constexpr int META_OFF = 4096;
-constexpr int ROT_HEAD_BYTES = 163840;  // fp32 R [128][128] + 3 x bf16 [128][128]
+constexpr int ROT_TERMS_OFF = D * D * 4;                 // 3 x bf16 [128][128] terms of R^T
+constexpr int ROT_NMU_OFF = ROT_TERMS_OFF + 3 * D * D * 2;  // fp32 [128] -(mu . R), the key mean's shift
+constexpr int ROT_HEAD_BYTES = ROT_NMU_OFF + D * 4;       // fp32 R [128][128] first
 
 // ---------------------------------------------------------------- page layout
 

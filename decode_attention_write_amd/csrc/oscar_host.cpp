@@ -51,6 +51,8 @@ struct oscar_kv {
   int32_t write_evicts = 0;    // 1: a write that overflows a non-empty window evicts as it goes
   int32_t out_bf16 = 0;        // 1: decode outputs are written as bf16
   bool has_rotation = false;
+  std::vector<float> rot_host;  // [hkv][128][128], kept for re-deriving the key-mean shift
+  std::vector<float> key_mean;  // [hkv][128], empty: no key mean
   // A HIP failure after a call has committed its host bookkeeping (page table mirror, FIFO,
   // lengths) leaves the mirror ahead of the device: the handle then refuses every further call.
   bool broken = false;
@@ -459,26 +461,24 @@ int oscar_kv_create(const oscar_kv_desc* d, const int32_t* free_pages, int32_t n
 
 void oscar_kv_destroy(oscar_kv* kv) { delete kv; }
 
-int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
-  if (!kv || !rot_host) { set_error("oscar_kv_set_rotation: null argument"); return OSCAR_E_ARG; }
-  if (int rc = check_usable(kv, "oscar_kv_set_rotation")) return rc;
+// The device rotation block of every head from the handle's host rotation and key mean: fp32 R,
+// three bf16 terms r0 + r1 + r2 ~= R (r0 = bf16(R), r1 = bf16(R - r0), r2 = bf16(R - r0 - r1); the
+// fp32 differences are exact, |R - r0 - r1 - r2| <= 2^-24 |R|) stored transposed ([term][output
+// channel c][input channel i]) for the write kernel's MFMA A operand, then fp32 -(mu . R) (the dot
+// products in fp64, rounded once; +0 where zero, so that a zero mean leaves every sum as it is).
+// Uploaded on stream; returns after the copy has consumed the host buffer.
+static int upload_rotation(oscar_kv* kv, void* stream, const char* who) {
   const int hkv = kv->desc.num_kv_heads;
-  const size_t n = static_cast<size_t>(hkv) * OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
-  for (size_t i = 0; i < n; ++i)
-    if (!std::isfinite(rot_host[i])) { set_error("oscar_kv_set_rotation: non-finite entry"); return OSCAR_E_NUMERIC; }
-  if (kv->plan_only) { kv->has_rotation = true; return OSCAR_OK; }
-  // per head: fp32 R, then three bf16 terms r0 + r1 + r2 ~= R (r0 = bf16(R), r1 = bf16(R - r0),
-  // r2 = bf16(R - r0 - r1); the fp32 differences are exact, |R - r0 - r1 - r2| <= 2^-24 |R|), stored
-  // transposed ([term][output channel c][input channel i]) for the write kernel's MFMA A operand
-  std::vector<uint8_t> blob(static_cast<size_t>(hkv) * OSCAR_ROT_HEAD_BYTES, 0);
   const size_t dd = OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
+  std::vector<uint8_t> blob(static_cast<size_t>(hkv) * OSCAR_ROT_HEAD_BYTES, 0);
   for (int h = 0; h < hkv; ++h) {
+    const float* rh = kv->rot_host.data() + h * dd;
     uint8_t* base = blob.data() + static_cast<size_t>(h) * OSCAR_ROT_HEAD_BYTES;
-    std::memcpy(base, rot_host + h * dd, dd * 4);
+    std::memcpy(base, rh, dd * 4);
     uint16_t* terms = reinterpret_cast<uint16_t*>(base + dd * 4);
     for (size_t i = 0; i < OSCAR_HEAD_DIM; ++i)
       for (size_t c = 0; c < OSCAR_HEAD_DIM; ++c) {
-        const float r = rot_host[h * dd + i * OSCAR_HEAD_DIM + c];
+        const float r = rh[i * OSCAR_HEAD_DIM + c];
         const uint16_t t0 = f32_to_bf16_rn(r);
         const float d1 = r - bf16_to_f32(t0);
         const uint16_t t1 = f32_to_bf16_rn(d1);
@@ -487,13 +487,51 @@ int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
         terms[dd + c * OSCAR_HEAD_DIM + i] = t1;
         terms[2 * dd + c * OSCAR_HEAD_DIM + i] = t2;
       }
+    float* nmu = reinterpret_cast<float*>(base + dd * 4 + 3 * dd * 2);
+    for (size_t c = 0; c < OSCAR_HEAD_DIM; ++c) {
+      double m = 0.0;
+      if (!kv->key_mean.empty())
+        for (size_t i = 0; i < OSCAR_HEAD_DIM; ++i)
+          m += static_cast<double>(kv->key_mean[h * OSCAR_HEAD_DIM + i]) * static_cast<double>(rh[i * OSCAR_HEAD_DIM + c]);
+      const float v = static_cast<float>(-m);
+      nmu[c] = (v == 0.0f) ? 0.0f : v;
+    }
   }
   hipError_t e = hipMemcpyAsync(kv->desc.rot, blob.data(), blob.size(), hipMemcpyHostToDevice, as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e, "oscar_kv_set_rotation: upload");
+  if (e != hipSuccess) return hip_fail(e, who);
   // the host blob dies at return: make sure the (pageable) copy has consumed it
   e = hipStreamSynchronize(as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e, "oscar_kv_set_rotation: sync");
+  if (e != hipSuccess) return hip_fail(e, who);
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_rotation(oscar_kv* kv, const float* rot_host, void* stream) {
+  if (!kv || !rot_host) { set_error("oscar_kv_set_rotation: null argument"); return OSCAR_E_ARG; }
+  if (int rc = check_usable(kv, "oscar_kv_set_rotation")) return rc;
+  const int hkv = kv->desc.num_kv_heads;
+  const size_t n = static_cast<size_t>(hkv) * OSCAR_HEAD_DIM * OSCAR_HEAD_DIM;
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(rot_host[i])) { set_error("oscar_kv_set_rotation: non-finite entry"); return OSCAR_E_NUMERIC; }
+  kv->rot_host.assign(rot_host, rot_host + n);
+  if (!kv->plan_only)
+    if (int rc = upload_rotation(kv, stream, "oscar_kv_set_rotation: upload")) return rc;
   kv->has_rotation = true;
+  return OSCAR_OK;
+}
+
+int oscar_kv_set_key_mean(oscar_kv* kv, const float* mean, void* stream) {
+  if (!kv) { set_error("oscar_kv_set_key_mean: null handle"); return OSCAR_E_ARG; }
+  if (int rc = check_usable(kv, "oscar_kv_set_key_mean")) return rc;
+  const size_t n = static_cast<size_t>(kv->desc.num_kv_heads) * OSCAR_HEAD_DIM;
+  if (mean) {
+    for (size_t i = 0; i < n; ++i)
+      if (!std::isfinite(mean[i])) { set_error("oscar_kv_set_key_mean: non-finite entry"); return OSCAR_E_ARG; }
+    kv->key_mean.assign(mean, mean + n);
+  } else {
+    kv->key_mean.clear();
+  }
+  if (kv->has_rotation && !kv->plan_only)
+    return upload_rotation(kv, stream, "oscar_kv_set_key_mean: upload");
   return OSCAR_OK;
 }
 

@@ -81,18 +81,20 @@ __device__ inline void step_write_block(const StepArgs& a, int kvh, int sl) {
   __shared__ float kin[D];
   const size_t src = (static_cast<size_t>(sq.src) * a.hkv + kvh) * D;
   float rc[D];
+  float shift = 0.0f;
   uint16_t vraw = 0;
   if (tid < D) {
     const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
 #pragma unroll
     for (int i = 0; i < D; ++i) rc[i] = rot[i * D + tid];   // column tid of R
+    shift = rot[ROT_NMU_OFF / 4 + tid];                       // -(mu . R)_tid, the key mean's shift
     kin[tid] = bf16_to_f32(a.k[src + tid]);
     vraw = a.v[src + tid];
   }
   if (sq.evict) evict_one(a.pool, a.ring, a.page_table, a.hkv, a.max_pages, sq.seq, kvh, sq.n_int2, codes, meta);
   __syncthreads();
   if (tid < D) {
-    float acc = 0.0f;
+    float acc = shift;
 #pragma unroll
     for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
     const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;

@@ -10,9 +10,12 @@
 #include <type_traits>
 
 #include "common.h"
+#include "oscar.h"
 #include "step_write.h"
 
 namespace oscar {
+
+static_assert(ROT_HEAD_BYTES == OSCAR_ROT_HEAD_BYTES, "rotation block layout");
 
 // ------------------------------------------------------------------ utilities
 
@@ -59,10 +62,10 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 // operand is R^T as three bf16 terms r0 = bf16(R^T), r1 = bf16(R^T - r0), r2 = bf16(R^T - r0 - r1),
 // so |R^T - r0 - r1 - r2| <= 2^-24 |R^T|; the B operand is the bf16 key tile as it is.  The
 // products are exact in fp32 and accumulate in fp32 (12 instructions of 32 products each, the
-// small terms first).  Wave w owns output channels 16 w .. 16 w + 15 of all 64 tokens and keeps
-// its A operand in registers for all tiles of the work-group; lane (q4, n16) holds channels
-// 16 w + 4 q4 + e (e = 0..3) of the tokens 16 nt + n16 (nt = 0..3), and reads the values of the
-// same positions from the value tile.
+// small terms first), starting from -(mu . R) when a key mean mu is set (zero otherwise).  Wave w
+// owns output channels 16 w .. 16 w + 15 of all 64 tokens and keeps its A operand in registers for
+// all tiles of the work-group; lane (q4, n16) holds channels 16 w + 4 q4 + e (e = 0..3) of the
+// tokens 16 nt + n16 (nt = 0..3), and reads the values of the same positions from the value tile.
 //
 // Quantization works in that register layout.  Range per (token, 64-channel group): each lane
 // reduces its 4 channels, the 4 rows of a wave are combined by lane swaps (v_permlane32_swap,
@@ -255,9 +258,12 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
   __shared__ v2f_w part[2][4][2][PAGE];    // (min, max) per (K/V, wave of the group, group, token)
   __shared__ v2f_w prm[2][PAGE][2];        // (fp32 minimum, 1/scale) per (K/V, token, group)
   __shared__ int need_clamp[4];            // per parameter wave: some level may fall outside [0, 3]
+  __shared__ float nmu[D];                 // -(mu . R): the key mean's shift, starts every accumulator
 
   // A operands: R^T rows 16 w + n16, 4 K-steps of 32 input channels, 3 terms
-  const uint16_t* terms = reinterpret_cast<const uint16_t*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES + D * D * 4);
+  const uint8_t* rblk = a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES;
+  const uint16_t* terms = reinterpret_cast<const uint16_t*>(rblk + ROT_TERMS_OFF);
+  if (tid < D) nmu[tid] = reinterpret_cast<const float*>(rblk + ROT_NMU_OFF)[tid];  // read after the first barrier
   v8bf_w aop[4][3];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -330,15 +336,17 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
     const int page = (n_q > 0) ? ptab[tile - 1] : 0;
     __syncthreads();  // the tile is in LDS
 
-    // rotation: 4 token columns of 16; values of the same positions
+    // rotation: 4 token columns of 16, each accumulator starting from the key mean's shift; values
+    // of the same positions
     v4f_w acc[4];
     v2u_w vp[4];
+    const v4f_w shift = *reinterpret_cast<const v4f_w*>(&nmu[16 * wave + 4 * q4]);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       v8bf_w b[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) b[ks] = *reinterpret_cast<const v8bf_w*>(&tk[16 * nt + n16][32 * ks + 8 * q4]);
-      acc[nt] = v4f_w{0.0f, 0.0f, 0.0f, 0.0f};
+      acc[nt] = shift;
 #pragma unroll
       for (int t = 2; t >= 0; --t)
 #pragma unroll
@@ -476,12 +484,13 @@ __global__ __launch_bounds__(128) void k_append(WriteArgs a) {
   float rc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) rc[i] = rot[i * D + c];   // column c of R, kept in registers
+  const float shift = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES + ROT_NMU_OFF)[c];
   for (int t = 0; t < a.n_new; ++t) {
     const size_t src = (static_cast<size_t>(sq.src) * a.n_new + t) * row + kvh * D;
     __syncthreads();
     kin[c] = bf16_to_f32(a.k[src + c]);
     __syncthreads();
-    float acc = 0.0f;
+    float acc = shift;  // -(mu . R)_c: the key mean's shift (+0 without a mean)
 #pragma unroll
     for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
     const int p = sq.len0 + t;

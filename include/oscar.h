@@ -67,7 +67,7 @@ extern "C" {
 #define OSCAR_WINDOW_TOKENS   256
 #define OSCAR_RING_SLOTS      (OSCAR_SINK_TOKENS + OSCAR_WINDOW_TOKENS)
 #define OSCAR_HEAD_BLOCK      5120   /* bytes of one KV head in one page */
-#define OSCAR_ROT_HEAD_BYTES  163840 /* bytes of one KV head's rotation block */
+#define OSCAR_ROT_HEAD_BYTES  164352 /* bytes of one KV head's rotation block */
 #define OSCAR_MAX_GQA         8      /* Hq / Hkv must be 1, 2, 4 or 8 */
 
 enum {
@@ -122,7 +122,10 @@ typedef struct oscar_kv oscar_kv;
  *             oscar_kv_set_rotation: per KV head R_K fp32 [128][128] followed by
  *             three bf16 [128][128] terms of R_K^T (term t, output channel c,
  *             input channel i; r0 = bf16(R^T), r1 = bf16(R^T - r0),
- *             r2 = bf16(R^T - r0 - r1), whose sum is R^T within 2^-24 of it).
+ *             r2 = bf16(R^T - r0 - r1), whose sum is R^T within 2^-24 of it),
+ *             then fp32 [128] -(mu . R_K) for the key mean mu set by
+ *             oscar_kv_set_key_mean (+0 where that is zero; all +0 without a
+ *             mean).
  */
 typedef struct {
     int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads with Hq/Hkv <= 8 */
@@ -355,6 +358,19 @@ int oscar_kv_free_pages(const oscar_kv *kv, int32_t *count, int32_t *host_out);
 /* Empty one sequence: its pages go to the FIFO tail in ascending logical order;
  * its device page-table row is reset to -1 on stream. */
 int oscar_kv_reset_seq(oscar_kv *kv, int32_t seq, void *stream);
+
+/* Key-mean subtraction on write (gist.science summary of OptR, section
+ * "해결책: OptR (출력 인지 회전)", step 1: keys are centred by a per-head mean
+ * before the rotation; a query's scores all move by the same q . mu, which the
+ * softmax cancels, so attention is unchanged while the INT2 groups see
+ * centred keys).  mean: host fp32 [num_kv_heads][128], finite, or NULL to
+ * remove the mean.  Every key written after the call (multi-token writes,
+ * appends, decode-step writes) is stored as (k - mu) . R_K; keys already in
+ * the cache keep the mean they were written with, so set it before the first
+ * write of a sequence.  The mean is kept on the host and, once a rotation is
+ * set, uploaded on stream (the call waits for the upload); setting a new
+ * rotation re-applies it.  OSCAR_E_ARG for a non-finite entry. */
+int oscar_kv_set_key_mean(oscar_kv *kv, const float *mean, void *stream);
 
 /* Decode tuning: pages_per_split = 0 picks a split size from the batch. */
 int oscar_kv_set_decode_split(oscar_kv *kv, int32_t pages_per_split);

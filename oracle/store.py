@@ -19,6 +19,12 @@ Readings taken where the pages are silent:
 * Sink and window keys are stored as bf16(k . R_K) (fp64 product, one
   rounding).  INT2 keys written by that first write are quantized from
   fp32(k . R_K).  Values are stored / quantized as given.
+* Optional key mean (gist.science summary of OptR, section "해결책: OptR (출력
+  인지 회전)", step 1: keys centred before the rotation): with a per-KV-head
+  mean mu set, every key written afterwards enters as (k - mu) . R_K in fp64
+  (subtraction, then the product) and is stored / quantized from that.
+  Queries are rotated by R_K alone: each query's scores all move by
+  -q . mu, which the softmax removes (attention-exact; pinned to 1e-12).
 * Eviction moves the oldest window token (position 64 + n_int2) to INT2 index
   n_int2, quantizing from its stored bf16 key and value.
 * Window token at position p sits in ring slot 64 + ((p - 64) mod 256);
@@ -30,7 +36,8 @@ Readings taken where the pages are silent:
   needs, or would overfill a window, changes nothing.
 
 Parity: pinned (store invariants, BF16 share, allocator order, bf16-only store
-against unquantized attention, eviction of a known token).
+against unquantized attention, eviction of a known token, attention-exactness of
+the key mean).
 """
 from __future__ import annotations
 
@@ -66,6 +73,15 @@ def to_bf16_bits_f64(x) -> np.ndarray:
     return out
 
 
+def rotate_keys(k64, rot, key_mean=None) -> np.ndarray:
+    """The write path's key transform in fp64: (k - mu) . R_K per KV head, or k . R_K without a
+    mean.  k64: [n, Hkv, 128]; rot: [Hkv, 128, 128]; key_mean: [Hkv, 128] or None."""
+    k = np.asarray(k64, dtype=np.float64)
+    if key_mean is not None:
+        k = k - np.asarray(key_mean, dtype=np.float32).astype(np.float64)[None]
+    return np.matmul(k.transpose(1, 0, 2), np.asarray(rot, dtype=np.float64)).transpose(1, 0, 2)
+
+
 def bf16_to_f64(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
@@ -87,6 +103,11 @@ class OracleStore:
         self.n_int2 = np.zeros(max_seqs, dtype=np.int64)
         # a write that overflows a non-empty window evicts token by token (else "window full")
         self.write_evicts = False
+        self.key_mean = None          # [Hkv, 128] fp32 or None
+
+    def set_key_mean(self, mean):
+        """Per-KV-head key mean subtracted from every key written afterwards (None: none)."""
+        self.key_mean = None if mean is None else np.asarray(mean, dtype=np.float32).reshape(self.hkv, D).copy()
 
     # ------------------------------------------------------------------ helpers
     def window_count(self, seq):
@@ -149,7 +170,7 @@ class OracleStore:
         for b, s in enumerate(seq_ids):
             L0 = int(self.length[s])
             k64 = bf16_to_f64(k_bits[b])                          # [n_new, Hkv, d]
-            x = np.matmul(k64.transpose(1, 0, 2), self.rot).transpose(1, 0, 2)   # k . R_K per head, fp64
+            x = rotate_keys(k64, self.rot, self.key_mean)         # (k - mu) . R_K per head, fp64
             kx_bf = to_bf16_bits_f64(x)
             if L0 == 0:
                 L = n_new

@@ -56,17 +56,21 @@ def fp16_ulp_diff(a, b):
     return np.abs(key(a) - key(b))
 
 
-def rotation_error_bound(k_bits, rot_h):
-    """Per-element bound on |x_gpu - k.R| for keys rotated on the matrix cores (bf16 [n, 128] keys,
-    one head's fp32 R).  The write kernel carries R^T as three bf16 terms r0 = bf16(R^T), r1 =
-    bf16(R^T - r0), r2 = bf16(R^T - r0 - r1), so |R - r0 - r1 - r2| <= 2^-24 |R| (bf16 unit
-    roundoff 2^-8, three times); the bf16 keys enter as they are; the products are exact in fp32
-    and the 384 of them go through 12 matrix instructions of 32 into an fp32 accumulator: up to 48
-    roundings of at most (1 + 2^-7) sum_i |k_i R_ij| each are allowed.  Products or inputs below
-    the fp32 normal range may be flushed: 2^-116 absolute covers 384 of them.  Returns [n, 128]."""
+def rotation_error_bound(k_bits, rot_h, mean=None):
+    """Per-element bound on |x_gpu - (k - mu).R| for keys rotated on the matrix cores (bf16 [n, 128]
+    keys, one head's fp32 R, optional key mean mu).  The write kernel carries R^T as three bf16
+    terms r0 = bf16(R^T), r1 = bf16(R^T - r0), r2 = bf16(R^T - r0 - r1), so |R - r0 - r1 - r2| <=
+    2^-24 |R| (bf16 unit roundoff 2^-8, three times); the bf16 keys enter as they are; the
+    accumulator starts from fp32(-(mu . R)) (within 2^-24 |mu . R|; zero without a mean); the
+    products are exact in fp32 and the 384 of them go through 12 matrix instructions of 32 into
+    the fp32 accumulator: up to 48 roundings of at most (1 + 2^-7) sum_i |k_i R_ij| + |mu . R|_j
+    each are allowed.  Products or inputs below the fp32 normal range may be flushed: 2^-116
+    absolute covers 384 of them.  Returns [n, 128]."""
     k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
     r = np.asarray(rot_h, np.float32).astype(np.float64)
-    return (np.abs(k) @ np.abs(r)) * (2.0 ** -24 + 48 * (1 + 2.0 ** -7) * 2.0 ** -24) + 2.0 ** -116
+    kr = np.abs(k) @ np.abs(r)
+    m = _shift_abs(rot_h, mean)[None]
+    return kr * 2.0 ** -24 + 48 * 2.0 ** -24 * ((1 + 2.0 ** -7) * kr + m) + 2.0 ** -24 * m + 2.0 ** -116
 
 
 def _ulp32(x):
@@ -179,14 +183,24 @@ def oracle_decode_on(pool, ring, table, length, n_int2, rot, q_bits, seq_ids, sm
     return attention.decode(pool, ring, table, length, n_int2, rot, q_bits, seq_ids, sm_scale, hq)
 
 
-def rotated_keys_f64(k_bits, rot):
-    """k . R_K in fp64 for bf16 keys [n, 128] and one head's fp32 rotation."""
-    return synth.bf16_bits_to_f32(k_bits).astype(np.float64) @ np.asarray(rot, np.float32).astype(np.float64)
+def rotated_keys_f64(k_bits, rot, mean=None):
+    """(k - mu) . R_K in fp64 for bf16 keys [n, 128], one head's fp32 rotation and optional fp32
+    key mean [128] (the oracle's rotate_keys for one head)."""
+    k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
+    return ostore.rotate_keys(k[:, None, :], np.asarray(rot, np.float32)[None],
+                              None if mean is None else np.asarray(mean, np.float32)[None])[:, 0, :]
 
 
-def quant_input_k(k_bits, rot):
-    """What the oracle quantizes for prefill INT2 keys: fp32(k . R_K)."""
-    return rotated_keys_f64(k_bits, rot).astype(np.float32).astype(np.float64)
+def quant_input_k(k_bits, rot, mean=None):
+    """What the oracle quantizes for prefill INT2 keys: fp32((k - mu) . R_K)."""
+    return rotated_keys_f64(k_bits, rot, mean).astype(np.float32).astype(np.float64)
+
+
+def _shift_abs(rot_h, mean):
+    """|mu . R| per output channel [128] (zeros without a mean)."""
+    if mean is None:
+        return np.zeros(128)
+    return np.abs(np.asarray(mean, np.float32).astype(np.float64) @ np.asarray(rot_h, np.float32).astype(np.float64))
 
 
 def oracle_store_for(hkv, max_seqs, max_pages, num_pages, free, rot):
@@ -220,18 +234,20 @@ def check_evicted(pool, table, ring_before, seq, n2, heads=None):
     return explained
 
 
-def ring_key_bound(k_bits, rot_h):
-    """Allowed |stored bf16 key - exact k.R| per channel, besides half a bf16 ulp of the stored value.
-    Multi-token writes rotate on the matrix cores (rotation_error_bound: bf16 terms of R^T within
-    2^-24 of it, exact products, fp32 accumulation); single-token appends use a 128-term fp32 dot
-    product.  Both stay within gamma_256 (1 + 2^-8) sum_i |k_i R_ij| + 2^-24 sum_i |k_i R_ij| +
+def ring_key_bound(k_bits, rot_h, mean=None):
+    """Allowed |stored bf16 key - exact (k - mu).R| per channel, besides half a bf16 ulp of the
+    stored value.  Multi-token writes rotate on the matrix cores (rotation_error_bound: bf16 terms
+    of R^T within 2^-24 of it, exact products, fp32 accumulation from fp32(-(mu . R)));
+    single-token appends use a 128-term fp32 dot product from the same start.  Both stay within
+    gamma_256 (1 + 2^-8) (sum_i |k_i R_ij| + |mu . R|_j) + 2^-24 (sum_i |k_i R_ij| + |mu . R|_j) +
     2^-116 (dot-product forward-error bound, Higham, Accuracy and Stability of Numerical
-    Algorithms, section 3.1).  Returns (bound, exact k.R) [n, 128]."""
+    Algorithms, section 3.1).  Returns (bound, exact (k - mu).R) [n, 128]."""
     k = synth.bf16_bits_to_f32(k_bits).astype(np.float64)
     r = np.asarray(rot_h, np.float32).astype(np.float64)
     u = 2.0 ** -24
     gamma = 256 * u / (1 - 256 * u)
-    return np.abs(k) @ np.abs(r) * (gamma * (1 + 2.0 ** -8) + 2.0 ** -24) + 2.0 ** -116, k @ r
+    a = np.abs(k) @ np.abs(r) + _shift_abs(rot_h, mean)[None]
+    return a * (gamma * (1 + 2.0 ** -8) + 2.0 ** -24) + 2.0 ** -116, rotated_keys_f64(k_bits, rot_h, mean)
 
 
 def bf16_ulp(x):
@@ -240,10 +256,10 @@ def bf16_ulp(x):
     return np.ldexp(1.0, e - 8)
 
 
-def check_ring_keys(got_bits, k_bits, rot_h):
+def check_ring_keys(got_bits, k_bits, rot_h, mean=None):
     """Stored bf16 ring keys [n, 128] of one head within half a bf16 ulp plus ring_key_bound of
-    the exact k.R (asserts)."""
-    bound, xk = ring_key_bound(k_bits, rot_h)
+    the exact (k - mu).R (asserts)."""
+    bound, xk = ring_key_bound(k_bits, rot_h, mean)
     got = ostore.bf16_to_f64(got_bits)
     ulp = np.maximum(bf16_ulp(got), bf16_ulp(xk))
     assert np.all(np.abs(got - xk) <= 0.5 * ulp + bound)

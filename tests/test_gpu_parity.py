@@ -65,11 +65,12 @@ def _kv_batch(cfg, seqs, hkv, n, token0=0):
     return ks, vs
 
 
-def _check_state(gpu, ora, seqs, rot, inputs):
+def _check_state(gpu, ora, seqs, rot, inputs, mean=None):
     """Page tables exact; ring V bit-exact, ring K within the fp32 rotation error bound; INT2 pages
     written by the first (prefill) write under the tolerance rules.
 
     inputs[s] = (k_bits [n, Hkv, 128], v_bits, prefill_len): every token written to sequence s so far.
+    mean: the key mean [Hkv, 128] those tokens were written with, or None.
     """
     gpool, gring, gtable = gpu
     assert np.array_equal(gtable, ora.page_table)
@@ -84,7 +85,7 @@ def _check_state(gpu, ora, seqs, rot, inputs):
             slots = np.array([ora.ring_slot(int(p)) for p in positions])
             assert np.array_equal(gring[s, :, 1, slots], ora.ring[s, :, 1, slots]), s
             for h in range(ora.hkv):
-                parity.check_ring_keys(gring[s, h, 0, slots], kb[positions, h], rot[h])
+                parity.check_ring_keys(gring[s, h, 0, slots], kb[positions, h], rot[h], None if mean is None else mean[h])
                 k_ulp_flips += int((gring[s, h, 0, slots] != ora.ring[s, h, 0, slots]).sum())
         # prefill INT2 tokens only: evicted ones are checked bit-exactly by the callers against the
         # oracle run on the GPU's own ring (identical inputs)
@@ -92,11 +93,12 @@ def _check_state(gpu, ora, seqs, rot, inputs):
         if n_pre == 0:
             continue
         for h in range(ora.hkv):
-            xk = parity.quant_input_k(kb[64:64 + n_pre, h], rot[h])
+            mh = None if mean is None else mean[h]
+            xk = parity.quant_input_k(kb[64:64 + n_pre, h], rot[h], mh)
             xv = synth.bf16_bits_to_f32(vb[64:64 + n_pre, h]).astype(np.float64)
             rep = parity.compare_int2_unit(gpool, gtable, ora.pool, ora.page_table, s, h, h, n_pre, xk, xv,
                                            check_tail=(n_pre == n2),
-                                           k_bound=parity.rotation_error_bound(kb[64:64 + n_pre, h], rot[h]))
+                                           k_bound=parity.rotation_error_bound(kb[64:64 + n_pre, h], rot[h], mh))
             for k in totals:
                 totals[k] += rep[k]
     assert totals["unexplained"] == 0, totals
@@ -133,13 +135,15 @@ def test_generator_gpu_twin_bit_exact(gpu_lib):
 
 def test_rotation_blob_terms(gpu_lib):
     """The device rotation block of each KV head: fp32 R, then the bf16 terms r0 = bf16(R^T),
-    r1 = bf16(R^T - r0), r2 = bf16(R^T - r0 - r1) (round to nearest even)."""
+    r1 = bf16(R^T - r0), r2 = bf16(R^T - r0 - r1) (round to nearest even), then fp32 -(mu . R):
+    all +0 without a key mean, the fp64 product rounded once with one set."""
     _case("rotation blob")
     rot = parity.calibrate(synth.CFG_QWEN3_4B, 3, 2)
     st = _store(gpu_lib, 8, 2, 1, 4, 4, None, rot)
     import torch
     torch.cuda.synchronize()
     blob = st.rot.cpu().numpy().reshape(2, -1)
+    assert blob.shape[1] == 65536 + 3 * 32768 + 512
     for h in range(2):
         assert np.array_equal(blob[h, :65536].view(np.float32).reshape(128, 128), rot[h])
         rt = np.ascontiguousarray(rot[h].T.astype(np.float32))
@@ -147,8 +151,16 @@ def test_rotation_blob_terms(gpu_lib):
         d1 = rt - synth.bf16_bits_to_f32(t0)
         t1 = synth.f32_to_bf16_bits(d1)
         t2 = synth.f32_to_bf16_bits(d1 - synth.bf16_bits_to_f32(t1))
-        terms = blob[h, 65536:].view(np.uint16).reshape(3, 128, 128)
+        terms = blob[h, 65536:65536 + 3 * 32768].view(np.uint16).reshape(3, 128, 128)
         assert np.array_equal(terms[0], t0) and np.array_equal(terms[1], t1) and np.array_equal(terms[2], t2)
+        assert not blob[h, 65536 + 3 * 32768:].any()           # +0 bit patterns
+    mu = np.random.default_rng(3).standard_normal((2, 128)).astype(np.float32)
+    st.set_key_mean(mu)
+    torch.cuda.synchronize()
+    blob = st.rot.cpu().numpy().reshape(2, -1)
+    for h in range(2):
+        want = (-(mu[h].astype(np.float64) @ rot[h].astype(np.float64))).astype(np.float32)
+        assert np.array_equal(blob[h, 65536 + 3 * 32768:].view(np.float32), want)
 
 
 def test_tiny_config_write_and_decode(gpu_lib):
@@ -237,6 +249,61 @@ def test_evict_append_decode_cycle(gpu_lib):
             _e2e(out, ref, step)
     for s in seqs:
         assert st.seq_info(s) == (470, 470 - 320)
+
+
+def test_key_mean_write_steps_and_decode(gpu_lib):
+    """With a per-KV-head key mean set, every write path stores (k - mu) . R_K: the multi-token
+    write (state under the tolerance rules, the mean's shift in the rotation bound), the
+    decode-step write (eviction + one-token append: ring keys within the bound, evicted tokens
+    bit-exact against the oracle on the GPU's ring), and decode matches the oracle on identical
+    state and end to end.  Clearing the mean makes the next sequence's keys plain k . R_K."""
+    hkv, hq = 2, 8
+    seqs = [1, 0]
+    cfg = synth.CFG_QWEN3_4B
+    _case("key mean: multi-token write, decode-step writes, decode, mean cleared")
+    rot = parity.calibrate(cfg, 6, hkv)
+    kc, _ = _kv_batch(cfg, [5], hkv, 2048)                      # keys of another sequence
+    mu = (synth.bf16_bits_to_f32(kc[0]).astype(np.float64).mean(axis=0) + 0.25).astype(np.float32)
+    free = synth.page_permutation(cfg, 6, 24)
+    st = _store(gpu_lib, hq, hkv, 3, 8, 24, free, rot)
+    st.set_key_mean(mu)
+    ora = ostore.OracleStore(hkv, 3, 8, 24, free, rot)
+    ora.set_key_mean(mu)
+    lens = {1: 320 + 64 * 2 + 9, 0: 380}
+    n_steps = 5
+    ks, vs = _kv_batch(cfg, seqs, hkv, max(lens.values()) + n_steps)
+    for b, s in enumerate(seqs):
+        st.write([s], parity.to_dev_bf16(ks[b:b + 1, :lens[s]]), parity.to_dev_bf16(vs[b:b + 1, :lens[s]]))
+        ora.write([s], ks[b:b + 1, :lens[s]], vs[b:b + 1, :lens[s]])
+    _check_state(parity.export(st), ora, seqs, rot,
+                 {s: (ks[b, :lens[s]], vs[b, :lens[s]], lens[s]) for b, s in enumerate(seqs)}, mean=mu)
+    for step in range(n_steps):
+        kt = np.stack([ks[b, lens[s] + step] for b, s in enumerate(seqs)])
+        vt = np.stack([vs[b, lens[s] + step] for b, s in enumerate(seqs)])
+        ring_b = parity.export(st)[1]
+        st.decode_write(seqs, parity.to_dev_bf16(kt), parity.to_dev_bf16(vt))   # windows full: evict, append
+        for b, s in enumerate(seqs):
+            ora.evict([s], 1)
+            ora.write([s], kt[b:b + 1, None], vt[b:b + 1, None])
+        after = parity.export(st)
+        for s in seqs:
+            parity.check_evicted(after[0], after[2], ring_b, s, int(ora.n_int2[s]) - 1)
+    gpu = parity.export(st)
+    _check_state(gpu, ora, seqs, rot,
+                 {s: (ks[b, :lens[s] + n_steps], vs[b, :lens[s] + n_steps], lens[s]) for b, s in enumerate(seqs)},
+                 mean=mu)
+    q = synth.decode_queries(cfg, 6, 2, hq, hkv)
+    out = st.decode(seqs, parity.to_dev_bf16(q), SCALE).cpu().numpy()
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], ora.length, ora.n_int2, rot, q, seqs, SCALE, hq)
+    assert parity.rel_l2(out, iso) <= ISO_TOL
+    _e2e(out, attention.decode_store(ora, q, seqs, SCALE, hq), "key mean")
+    # mean cleared: a new sequence is written as k . R_K
+    st.set_key_mean(None)
+    ora.set_key_mean(None)
+    k2, v2 = _kv_batch(cfg, [2], hkv, 400)
+    st.write([2], parity.to_dev_bf16(k2), parity.to_dev_bf16(v2))
+    ora.write([2], k2, v2)
+    _check_state(parity.export(st), ora, [2], rot, {2: (k2[0], v2[0], 400)})
 
 
 def test_fused_decode_write_matches_evict_then_write(gpu_lib):

@@ -431,6 +431,53 @@ def test_decode_bf16_store_matches_unquantized_attention():
         assert np.linalg.norm(out[0, h] - other) / np.linalg.norm(other) > 0.3
 
 
+def test_key_mean_transform_is_attention_exact():
+    """The write path's key transform with a key mean, (k - mu) . R_K (oracle store.rotate_keys),
+    with queries rotated by R_K alone: every score of a query moves by the same -q . mu, so the
+    attention output equals plain attention over the raw keys to 1e-12 (gist.science summary of
+    OptR, solution section, step 1).  A per-token centring (each key minus its own channel mean)
+    is not exact: it is rejected."""
+    rng = np.random.default_rng(21)
+    r = np.linalg.qr(_rot()[0].astype(np.float64))[0]   # exactly orthogonal in fp64
+    k = rng.standard_normal((400, D)) * 1.5 + rng.standard_normal(D) * 4
+    v = rng.standard_normal((400, D))
+    mu = k.mean(axis=0).astype(np.float32)
+    x = store.rotate_keys(k[:, None, :], r[None], mu[None])[:, 0, :]
+    assert np.abs(x - (k - mu.astype(np.float64)) @ r).max() < 1e-12 * np.abs(x).max()
+    for _ in range(5):
+        q = rng.standard_normal(D)
+        o, _, _ = attention.attend(q, k, v, 1 / np.sqrt(D))
+        o_m, _, _ = attention.attend(q @ r, x, v, 1 / np.sqrt(D))
+        assert np.abs(o_m - o).max() <= 1e-12 * max(1.0, np.abs(o).max())
+        bad = (k - k.mean(axis=1, keepdims=True)) @ r
+        o_b, _, _ = attention.attend(q @ r, bad, v, 1 / np.sqrt(D))
+        assert np.abs(o_b - o).max() > 1e-3
+
+
+def test_decode_bf16_store_with_key_mean_matches_unquantized_attention():
+    """With a key mean set, an all-BF16 store (L <= 320) holds bf16((k - mu) . R_K) and decodes to
+    plain attention over the raw keys up to the bf16 rounding of the stored keys."""
+    rot = _rot(2)
+    n_q = 4
+    kb = np.stack([synth.unit_kv(synth.CFG_TINY, 0, 0, kv, 300)[0] for kv in range(2)], axis=1)
+    vb = np.stack([synth.unit_kv(synth.CFG_TINY, 0, 0, kv, 300)[1] for kv in range(2)], axis=1)
+    k = synth.bf16_bits_to_f32(kb).astype(np.float64)
+    v = synth.bf16_bits_to_f32(vb).astype(np.float64)
+    mu = (k.mean(axis=0) + 3.0).astype(np.float32)            # [2, 128], off the keys' centre
+    st = store.OracleStore(2, 1, 4, 4, range(4), rot)
+    st.set_key_mean(mu)
+    st.write([0], kb[None], vb[None])
+    want = store.to_bf16_bits_f64(store.rotate_keys(k, rot.astype(np.float64), mu))
+    assert np.array_equal(st.ring[0, :, 0, :300], want.transpose(1, 0, 2))
+    qb = synth.decode_queries(synth.CFG_TINY, 0, 1, n_q, 2)
+    out = attention.decode_store(st, qb, [0], 1 / np.sqrt(D), n_q)
+    q = synth.bf16_bits_to_f32(qb).astype(np.float64)
+    for h in range(n_q):
+        kv = h // 2
+        o, _, _ = attention.attend(q[0, h], k[:, kv], v[:, kv], 1 / np.sqrt(D))
+        assert np.linalg.norm(out[0, h] - o) / np.linalg.norm(o) < 2e-2, h
+
+
 def test_decode_gqa_mapping_uniform_scores():
     """Zero queries give uniform attention: head h returns the mean value of KV head h // g."""
     rot = np.stack([np.eye(D, dtype=np.float32)] * 2)
