@@ -129,7 +129,7 @@ def check_tensor(t, name, shape, dtypes, device=None):
     these pointers, so a wrong size, stride or element width would go out of bounds silently."""
     if t is None:
         raise ValueError(f"{name}: missing tensor")
-    if tuple(t.shape) != tuple(int(x) for x in shape):
+    if t.shape != shape and tuple(t.shape) != tuple(int(x) for x in shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
@@ -139,9 +139,15 @@ def check_tensor(t, name, shape, dtypes, device=None):
         raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
+_BF16_TYPES = None
+
+
 def _bf16_types():
-    import torch
-    return (torch.bfloat16, torch.int16, torch.uint16)   # bf16 values or their raw bits
+    global _BF16_TYPES
+    if _BF16_TYPES is None:
+        import torch
+        _BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)   # bf16 values or their raw bits
+    return _BF16_TYPES
 
 
 def _out_types(store):
@@ -156,14 +162,40 @@ def _check_ws(ws, device):
         raise ValueError(f"ws: on {ws.device}, expected {device}")
 
 
+def _current_raw_stream():
+    """torch's current stream on the current device as an integer handle.  The raw query costs a
+    tenth of a microsecond against about three for torch.cuda.current_stream(), which builds a
+    Python stream object: it dominated the host time of a one-token decode-step write."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(torch._C._cuda_getDevice())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream(stream):
     if stream is None:
-        import torch
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return ctypes.c_void_p(_current_raw_stream())
     return ctypes.c_void_p(int(stream))
 
 
+_I32_CACHE = {}
+
+
 def _i32(seq_ids):
+    """int32 array of sequence ids and its address.  Short id lists are cached by value (the
+    library only reads them), which saves building the array on every decode-step call."""
+    if isinstance(seq_ids, (list, tuple)) and len(seq_ids) <= 64:
+        key = tuple(seq_ids)
+        hit = _I32_CACHE.get(key)
+        if hit is not None:
+            return hit
+        a = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
+        a.setflags(write=False)
+        r = (a, a.ctypes.data_as(ctypes.c_void_p))
+        if len(_I32_CACHE) < 4096:
+            _I32_CACHE[key] = r
+        return r
     a = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int32))
     return a, a.ctypes.data_as(ctypes.c_void_p)
 
@@ -231,8 +263,9 @@ def oscar_kv_decode_write(store, seq_ids, k, v, stream=None):
     k, v: bf16 device tensors [n_seqs, Hkv, 128] (contiguous)."""
     ids, p = _i32(seq_ids)
     if not store.plan_only:
-        for t, name in ((k, "k"), (v, "v")):
-            check_tensor(t, name, (len(ids), store.hkv, HEAD_DIM), _bf16_types(), store.device)
+        shape = (len(ids), store.hkv, HEAD_DIM)
+        check_tensor(k, "k", shape, _bf16_types(), store.device)
+        check_tensor(v, "v", shape, _bf16_types(), store.device)
     _check(load().oscar_kv_decode_write(store.handle, p, len(ids), _ptr(k), _ptr(v),
                                         None if store.plan_only else _stream(stream)))
 
