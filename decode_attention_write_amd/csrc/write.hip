@@ -203,7 +203,7 @@ __device__ inline void write_codes(uint32_t* blk, const v4f_w* acc, const v4f_w*
   {
     // this lane's word after the swaps: token 16 t + n16 with t = [0, 2, 1, 3][row]
     const int t = ((q4 & 1) << 1) | (q4 >> 1);
-    __builtin_nontemporal_store(kword, &blk[(KC_OFF >> 2) + 256 * (t >> 1) + 4 * (16 * kq + n16) + 2 * (t & 1) + grp]);
+    blk[(KC_OFF >> 2) + 256 * (t >> 1) + 4 * (16 * kq + n16) + 2 * (t & 1) + grp] = kword;
   }
   // value words: code of (token 16 nt + n16, channel e) at bit 8 (nt >> 1) + vsh of the partial
   // word (e, nt & 1), summed over the 8 lanes of the half-row
@@ -238,7 +238,7 @@ __device__ inline void write_codes(uint32_t* blk, const v4f_w* acc, const v4f_w*
   // word of channel 16 w + 4 q4 + e, e = 2 sel2 + sel1, token quarter 2 sel0 + (n16 >> 3)
   const int e = 2 * static_cast<int>(sel2) + static_cast<int>(sel1);
   const int vq = 2 * static_cast<int>(sel0) + ((lane >> 3) & 1);
-  __builtin_nontemporal_store(vword, &blk[(VC_OFF >> 2) + 256 * grp + 4 * (16 * vq + 4 * q4 + e) + kq]);
+  blk[(VC_OFF >> 2) + 256 * grp + 4 * (16 * vq + 4 * q4 + e) + kq] = vword;
 }
 
 __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
@@ -274,8 +274,9 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * D * 2;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
   // A 64 x 128 bf16 tile (keys or values) moves global -> registers (2 x 16 bytes per thread) ->
-  // LDS.  Inputs are read once and the INT2 pages are not read back by this launch: both go with
-  // the non-temporal hint.  When a tile's buffers have been read, the next tile goes from the
+  // LDS.  Inputs are read once: they go with the non-temporal hint.  The INT2 words are stored as
+  // plain 4-byte stores, which the L2 merges into whole lines (with the non-temporal hint they
+  // reached memory as partial lines: 1.5 x the page bytes written, at the same speed).  When a tile's buffers have been read, the next tile goes from the
   // registers to LDS and the loads of the one after it are issued: in flight for a whole tile of
   // rotation and quantization.  Loads are never
   // conditional (rows past the call's tokens re-read the last row and are zeroed when stored; past
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
           inv = qp.inv;  // 0 when the stored scale is 0: every code is then 0
           mword = static_cast<uint32_t>(qp.s16) | (static_cast<uint32_t>(qp.lo16) << 16);
         }
-        __builtin_nontemporal_store(mword, &blk[(META_OFF >> 2) + t_]);
+        blk[(META_OFF >> 2) + t_] = mword;
         prm[isv][j][g] = v2f_w{lo, inv};
         // levels are monotone in x: if the group's smallest and largest values land in [0, 3]
         // unclamped, every value of the group does
