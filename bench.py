@@ -301,12 +301,15 @@ def prefill_leg(reps=5, cpu=True):
     # algorithmic matrix-core work: k . R_K per token-head (2 * 128 * 128 flop); the kernel runs
     # it twice (bf16 terms r0 + r1 of R_K)
     flop = 2 * 128 * 128 * L * hkv
-    # appends: evict the oldest window token into INT2, then write one token, per step
+    # appends: evict the oldest window token into INT2, then write one token, per step (the
+    # per-call input views are made before the timed loop: a caller holds its new token's tensor)
+    kviews = [kbuf[:, L + i] for i in range(PREFILL_APPENDS)]
+    vviews = [vbuf[:, L + i] for i in range(PREFILL_APPENDS)]
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for i in range(PREFILL_APPENDS):
-        st.decode_write([0], kbuf[:, L + i], vbuf[:, L + i])
+        st.decode_write([0], kviews[i], vviews[i])
     a1.record()
     torch.cuda.synchronize()
     st.set_timing(False)
