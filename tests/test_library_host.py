@@ -394,3 +394,27 @@ def test_noalloc_step_host_limits():
     assert st.step_workspace_bytes(ids[:4]) <= oscar.NOALLOC_SCRATCH_BYTES
     oscar.oscar_decode_step_noalloc(st, ids[:4], None, None, None, 0.1, None)
     assert st.seq_info(0) == (L + 1, L - 320 + 1)              # the step's write was planned
+
+
+def test_key_mean_host_checks():
+    """oscar_kv_set_key_mean: a null handle and a non-finite entry are refused (E_ARG, nothing
+    changes); a finite mean, clearing it (NULL) and setting it before or after the rotation are
+    accepted on a plan-only store."""
+    lib = oscar.load()
+    assert lib.oscar_kv_set_key_mean(None, None, None) == oscar.E_ARG
+    s = _plan_store()
+    mu = np.zeros((2, 128), np.float32)
+    s.set_key_mean(mu)                       # before the rotation: kept for it
+    s.set_rotation(np.stack([np.eye(128, dtype=np.float32)] * 2))
+    bad = mu.copy()
+    bad[1, 5] = np.nan
+    with pytest.raises(oscar.OscarError) as e:
+        s.set_key_mean(bad)
+    assert e.value.status == oscar.E_ARG and "non-finite" in str(e.value)
+    bad[1, 5] = np.inf
+    with pytest.raises(oscar.OscarError):
+        s.set_key_mean(bad)
+    s.set_key_mean(mu + 1.5)
+    s.set_key_mean(None)
+    s.write([0], None, None, n_new=400)      # the store still works
+    assert s.seq_info(0) == (400, 80)
