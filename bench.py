@@ -363,10 +363,12 @@ def prefill_leg(reps=5, cpu=True):
 
 def layer_leg(cfg, hq, hkv, lengths, reps, label, cpu_units=None):
     """One attention layer over sequences of the given lengths (one R_K per KV head, pages in a
-    seeded shuffled order): prefill writes, then `reps` decode steps (the decode-step write of
-    one token per sequence, then decode attention), each after one untimed step.  Returns the
-    split kernel's mean launch time (library events), the whole step's time and their rates, and
-    with cpu_units ((seq, KV head) list) the CPU-oracle decode leg on the final state (or None)."""
+    seeded shuffled order): prefill writes, one untimed decode step (the decode-step write of one
+    token per sequence, then decode attention), `reps` steps with the library's events around
+    the split kernel, then `reps` steps without them, timed as whole steps (an event pair inside a
+    step adds its own gaps).  Returns the split kernel's mean launch time, the whole step's time,
+    their difference and rates, and with cpu_units ((seq, KV head) list) the CPU-oracle decode
+    leg on the final state (or None)."""
     import numpy as np
     import torch
 
@@ -377,12 +379,12 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, cpu_units=None):
     B = len(lengths)
     rots = np.stack([oscar.oscar_calibrate_host(synth.bf16_bits_to_f32(synth.calibration_queries(cfg, 0, h)))[0]
                      for h in range(hkv)])
-    max_pages = -(-(max(lengths) + reps + 2) // 64) + 1
-    num_pages = sum(-(-(L + reps + 2) // 64) for L in lengths) + B
+    n_new = 2 * reps + 1
+    max_pages = -(-(max(lengths) + n_new + 1) // 64) + 1
+    num_pages = sum(-(-(L + n_new + 1) // 64) for L in lengths) + B
     st = oscar.KVStore(hq, hkv, B, max_pages, num_pages, free_pages=synth.page_permutation(cfg, 0, num_pages))
     st.set_rotation(rots)
     prm = sgpu.HeadParams(cfg, 0, hkv)
-    n_new = reps + 1
     kbuf = torch.empty((1, max(lengths) + n_new, hkv, 128), dtype=torch.int16, device="cuda")
     vbuf = torch.empty_like(kbuf)
     newk = torch.empty((n_new, B, hkv, 128), dtype=torch.int16, device="cuda")
@@ -413,17 +415,21 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, cpu_units=None):
     torch.cuda.synchronize()
     st.read_timing(oscar.TIMED_DECODE)
     info = [st.seq_info(s) for s in seqs]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     flush.fill_(1)
     for i in range(reps):
         flush.sum()
-        evs[i][0].record()
         step(1 + i)
-        evs[i][1].record()
     torch.cuda.synchronize()
     n, k_ms, each = st.read_timing(oscar.TIMED_DECODE, each=True)
     st.set_timing(False)
     assert n == reps * -(-B // 64), n
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        flush.sum()
+        evs[i][0].record()
+        step(1 + reps + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
     step_us = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
     kbytes = float(np.mean([split_kernel_bytes([L + i + 1 for L, _ in info], [n2 + i + 1 for _, n2 in info], hkv)
                             for i in range(reps)]))
@@ -436,10 +442,12 @@ def layer_leg(cfg, hq, hkv, lengths, reps, label, cpu_units=None):
         "split_kernel_gbps": round(kbytes / kernel_us / 1e3, 1),
         "split_kernel_pct_peak": round(100 * kbytes / kernel_us / 1e3 / PEAK_GBPS, 2),
         "step_us_median": round(float(np.median(step_us)), 2),
+        "step_overhead_us": round(float(np.median(step_us)) - float(np.median(each)) * 1e3, 2),
         "steps": reps,
     }
     log(f"{label}: split kernel {res['split_kernel_us']} us = {res['split_kernel_gbps']} GB/s "
-        f"({res['split_kernel_pct_peak']}% of 8 TB/s); step (write + attention) {res['step_us_median']} us")
+        f"({res['split_kernel_pct_peak']}% of 8 TB/s); step (write + attention) {res['step_us_median']} us, "
+        f"{res['step_overhead_us']} us above the split kernel")
     leg = None
     if cpu_units:
         st.decode(seqs, q, scale, out=out, ws=ws)

@@ -182,49 +182,70 @@ __global__ __launch_bounds__(256) void k_decode_simple(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
-// Grid (q heads, sequences of this chunk), 128 threads: out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// Grid (q heads, sequences of this chunk), 512 threads: out = sum_i 2^(m_i - M) o_i / sum_i
+// 2^(m_i - M) l_i over the unit's records i.  Thread (slice, c) takes channel c of the records
+// 16 slice + 64 k + j (j < 16) with a running maximum of its own, so that all 16 records' loads
+// of a pass are issued at once and nothing waits for a maximum over the whole unit; the four
+// slices are then merged.
 
-__global__ __launch_bounds__(128) void k_combine(DecodeArgs a) {
-  const int h = blockIdx.x, sl = blockIdx.y, c = threadIdx.x;
+constexpr int COMBINE_SLICES = 4, COMBINE_BATCH = 16;
+
+__global__ __launch_bounds__(COMBINE_SLICES * D) void k_combine(DecodeArgs a) {
+  const int h = blockIdx.x, sl = blockIdx.y, c = threadIdx.x & (D - 1), slice = threadIdx.x >> 7;
   const DecodeSeq sq = a.seqs[sl];
-  const int n_split = unit_records(sq.n_int2, sq.len, a.pages_per_split, a.kernel);
+  const int n = unit_records(sq.n_int2, sq.len, a.pages_per_split, a.kernel);
   const float* rec0 = a.part + (static_cast<size_t>(sl) * a.hq + h) * a.n_split_max * PART_STRIDE;
-  __shared__ float wsh[128];
-  __shared__ float red[2];
-  // split weights 2^(m_i - M), loaded in parallel (one split per thread, 128 at a time)
-  float M = -INFINITY;
-  for (int s0 = c; s0 < n_split; s0 += 128) M = fmaxf(M, rec0[static_cast<size_t>(s0) * PART_STRIDE]);
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int b = COMBINE_BATCH * slice; b < n; b += COMBINE_SLICES * COMBINE_BATCH) {
+    float m[COMBINE_BATCH], l[COMBINE_BATCH], o[COMBINE_BATCH];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  if ((c & 63) == 0) red[c >> 6] = M;
+    for (int j = 0; j < COMBINE_BATCH; ++j) {
+      const float* rec = rec0 + static_cast<size_t>(min(b + j, n - 1)) * PART_STRIDE;  // in range
+      m[j] = rec[0];
+      l[j] = rec[1];
+      o[j] = rec[2 + c];
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < COMBINE_BATCH; ++j)
+      if (b + j < n) mb = fmaxf(mb, m[j]);
+    if (mb == -INFINITY) continue;  // only empty records so far (m = -inf, l = 0, o = 0)
+    const float alpha = (M == -INFINITY) ? 0.0f : exp2f(M - mb);
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int j = 0; j < COMBINE_BATCH; ++j) {
+      const float w = (b + j < n && m[j] != -INFINITY) ? exp2f(m[j] - mb) : 0.0f;
+      L = fmaf(w, l[j], L);
+      O = fmaf(w, o[j], O);
+    }
+    M = mb;
+  }
+  __shared__ float sm[COMBINE_SLICES], sls[COMBINE_SLICES], so[COMBINE_SLICES][D];
+  if (c == 0) {
+    sm[slice] = M;
+    sls[slice] = L;
+  }
+  so[slice][c] = O;
   __syncthreads();
-  M = fmaxf(red[0], red[1]);
-  float L = 0.0f, O = 0.0f;
-  for (int b = 0; b < n_split; b += 128) {
-    __syncthreads();
-    const int s = b + c;
-    float w = 0.0f;
-    if (s < n_split) {
-      const float m = rec0[static_cast<size_t>(s) * PART_STRIDE];
-      w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-    }
-    wsh[c] = w;
-    __syncthreads();
-    const int nb = min(128, n_split - b);
-#pragma unroll 4
-    for (int i = 0; i < nb; ++i) {
-      const float* rec = rec0 + static_cast<size_t>(b + i) * PART_STRIDE;
-      L = fmaf(wsh[i], rec[1], L);
-      O = fmaf(wsh[i], rec[2 + c], O);
-    }
+  if (slice != 0) return;
+  float Mt = sm[0];
+#pragma unroll
+  for (int p = 1; p < COMBINE_SLICES; ++p) Mt = fmaxf(Mt, sm[p]);
+  float Lt = 0.0f, Ot = 0.0f;
+#pragma unroll
+  for (int p = 0; p < COMBINE_SLICES; ++p) {
+    const float w = (sm[p] == -INFINITY) ? 0.0f : exp2f(sm[p] - Mt);
+    Lt = fmaf(w, sls[p], Lt);
+    Ot = fmaf(w, so[p][c], Ot);
   }
   const size_t o = (static_cast<size_t>(sq.src) * a.hq + h) * D + c;
-  if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(O / L);
-  else a.out[o] = O / L;
+  if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(Ot / Lt);
+  else a.out[o] = Ot / Lt;
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(COMBINE_SLICES * D), 0, s, a);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct StepSeq {
   int32_t n_int2;  // INT2 count before the call
   int32_t src;     // row of this sequence in the call's k/v arrays
   int32_t evict;   // 1: the window is full, evict its oldest token first
+  int32_t page;    // with evict: physical page of INT2 index n_int2 (the evicted token's page)
 };
 
 struct StepArgs {

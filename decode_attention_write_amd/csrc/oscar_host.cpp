@@ -309,15 +309,16 @@ std::vector<StepSeq> commit_step_write(oscar_kv* kv, const int32_t* seq_ids, int
     const int s = seq_ids[i];
     const int64_t win = std::max<int64_t>(0, kv->len[s] - kSink - kv->n_int2[s]);
     const bool ev = (win == kWin);
-    plan[i] = StepSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), i, ev ? 1 : 0};
+    plan[i] = StepSeq{s, static_cast<int32_t>(kv->len[s]), static_cast<int32_t>(kv->n_int2[s]), i, ev ? 1 : 0, -1};
     if (ev) {
+      const int32_t idx = static_cast<int32_t>(s * maxp + kv->n_int2[s] / kPage);
       if (kv->n_int2[s] % kPage == 0) {
         const int32_t page = kv->fifo.front();
         kv->fifo.pop_front();
-        const int32_t idx = static_cast<int32_t>(s * maxp + kv->n_int2[s] / kPage);
         kv->table[idx] = page;
         upd.emplace_back(idx, page);
       }
+      plan[i].page = kv->table[idx];
       kv->n_int2[s] += 1;
     }
     kv->len[s] += 1;

@@ -13,23 +13,33 @@ namespace oscar {
 
 // ------------------------------------------------------------------ eviction
 // One token of one (sequence, KV head) moves from the window to INT2: INT2 index i takes ring
-// slot 64 + i % 256 (the oldest window token).  256 threads; uses LDS scratch codes/meta.
-__device__ inline void evict_one(uint8_t* pool, const uint16_t* ring, const int32_t* page_table, int hkv,
-                                 int max_pages, int seq, int kvh, int i, uint8_t (*codes)[D], uint16_t* meta) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// slot 64 + i % 256 (the oldest window token).  256 threads: thread t holds channel t % 128 of
+// the key (t < 128) or the value (t >= 128).
+
+// This thread's ring element of the token that INT2 index i evicts.
+__device__ inline float evict_value(const uint16_t* ring, int hkv, int seq, int kvh, int i) {
+  const int tid = threadIdx.x, isv = tid >> 7, c = tid & (D - 1);
   const size_t ring_head = (static_cast<size_t>(seq) * hkv + kvh) * 2 * RING * D;
+  return bf16_to_f32(ring[ring_head + (static_cast<size_t>(isv) * RING + SINK + (i % WIN)) * D + c]);
+}
+
+// Quantizes and stores the evicted token (xv: this thread's ring element, from evict_value) into
+// slot i % 64 of `page`.  A page's slot 0 clears the whole block first (pages are recycled);
+// later slots only add their bits: the key words and metadata of a token are whole words, the
+// value words hold 16 tokens each and take the token's codes by an atomic OR, so no word is read
+// back.  Uses LDS scratch codes/meta; ends with a barrier.
+__device__ inline void evict_one(uint8_t* pool, int hkv, int page, int kvh, int i, float xv, uint8_t (*codes)[D],
+                                 uint16_t* meta) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int slot = i & (PAGE - 1);
-  const int page = page_table[static_cast<size_t>(seq) * max_pages + i / PAGE];
   uint32_t* blk = reinterpret_cast<uint32_t*>(pool + (static_cast<size_t>(page) * hkv + kvh) * HEAD_BLOCK);
   if (slot == 0) {
     for (int w = tid; w < HEAD_BLOCK / 4; w += 256) blk[w] = 0;
     __threadfence_block();
   }
   __syncthreads();
-  const int rs = SINK + (i % WIN);
   // wave wv: task (isv = wv >> 1, group = wv & 1); lane holds one channel
   const int isv = wv >> 1, g = wv & 1, c = 64 * g + lane;
-  const float xv = bf16_to_f32(ring[ring_head + (static_cast<size_t>(isv) * RING + rs) * D + c]);
   float mn = xv, mx = xv;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -53,11 +63,11 @@ __device__ inline void evict_one(uint8_t* pool, const uint16_t* ring, const int3
     }
     blk[(KC_OFF >> 2) + kc_word(slot, 64 * gg + 16 * kq)] = word;
   } else if (tid < 8 + D) {
-    // value word of channel cc: read-modify-write of this token's 2 bits
+    // value word of channel cc: this token's 2 bits, whose place is still zero
     const int cc = tid - 8;
-    uint32_t* wp = blk + (VC_OFF >> 2) + vc_word(slot, cc);
-    const int b = vc_bit(slot);
-    *wp = (*wp & ~(3u << b)) | (static_cast<uint32_t>(codes[1][cc]) << b);
+    const uint32_t bits = static_cast<uint32_t>(codes[1][cc]) << vc_bit(slot);
+    if (bits != 0)
+      __hip_atomic_fetch_or(blk + (VC_OFF >> 2) + vc_word(slot, cc), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else if (tid < 8 + D + 4) {
     const int m = tid - 8 - D;
     blk[(META_OFF >> 2) + 4 * slot + m] = static_cast<uint32_t>(meta[2 * m]) | (static_cast<uint32_t>(meta[2 * m + 1]) << 16);
@@ -68,11 +78,12 @@ __device__ inline void evict_one(uint8_t* pool, const uint16_t* ring, const int3
 
 // ------------------------------------------------------------------ decode-step write
 // One (KV head, sequence of the chunk) per 256-thread work-group: the eviction of k_evict (when
-// the window is full) and the single-token append of k_append.  The new token's loads
-// (key, value, column c of R_K for thread c < 128) are issued first so that their latency
-// overlaps the eviction; the new token lands in the ring slot the eviction has just read
-// (window position 64 + n_int2 + 256 maps to slot 64 + n_int2 % 256), so it is written only
-// after the eviction's barrier.
+// the window is full) and the single-token append of k_append.  Every load is issued first
+// (the evicted token's ring element, and for thread c < 128 the new token's key and value and
+// column c of R_K), so the step waits for memory once; the evicted token's page comes with the
+// plan.  The new token lands in the ring slot the eviction has just read (window position
+// 64 + n_int2 + 256 maps to slot 64 + n_int2 % 256), so it is written only after the eviction's
+// barriers.
 __device__ inline void step_write_block(const StepArgs& a, int kvh, int sl) {
   const int tid = threadIdx.x;
   const StepSeq sq = a.seqs[sl];
@@ -91,7 +102,8 @@ __device__ inline void step_write_block(const StepArgs& a, int kvh, int sl) {
     kin[tid] = bf16_to_f32(a.k[src + tid]);
     vraw = a.v[src + tid];
   }
-  if (sq.evict) evict_one(a.pool, a.ring, a.page_table, a.hkv, a.max_pages, sq.seq, kvh, sq.n_int2, codes, meta);
+  const float xv = sq.evict ? evict_value(a.ring, a.hkv, sq.seq, kvh, sq.n_int2) : 0.0f;
+  if (sq.evict) evict_one(a.pool, a.hkv, sq.page, kvh, sq.n_int2, xv, codes, meta);
   __syncthreads();
   if (tid < D) {
     float acc = shift;

@@ -513,8 +513,12 @@ __global__ __launch_bounds__(256) void k_evict(EvictArgs a) {
   const EvictSeq sq = a.seqs[sl];
   __shared__ uint8_t codes[2][D];
   __shared__ uint16_t meta[8];
-  for (int e = 0; e < a.n_evict; ++e)
-    evict_one(a.pool, a.ring, a.page_table, a.hkv, a.max_pages, sq.seq, kvh, sq.n_int2 + e, codes, meta);
+  const int32_t* ptab = a.page_table + static_cast<size_t>(sq.seq) * a.max_pages;
+  for (int e = 0; e < a.n_evict; ++e) {
+    const int i = sq.n_int2 + e;
+    const float xv = evict_value(a.ring, a.hkv, sq.seq, kvh, i);
+    evict_one(a.pool, a.hkv, ptab[i / PAGE], kvh, i, xv, codes, meta);
+  }
 }
 
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s) {
