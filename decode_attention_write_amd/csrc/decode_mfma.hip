@@ -213,16 +213,18 @@ __device__ inline int vcode_exp(int p) {
 
 // ------------------------------------------------------------------ BF16 sink + window split
 // One wavefront over 64-slot chunks [ch0, ch1) of the ring (a range without any token writes the
-// empty record m = -inf, l = 0, o = 0).  Scores: lane = ring slot, the lane reads
-// its own key row (all sixteen 16-byte pieces in flight at once).  Value product: lane = channel
-// pair, token rows read in batches of 16 so that 16 loads are in flight.  Slots that hold no
-// token are masked by a wave-uniform ballot; their (possibly uninitialised) rows never reach
-// the sums.
+// empty record m = -inf, l = 0, o = 0).  Scores: lane = ring slot, the lane reads its own key
+// row in batches of KB 16-byte pieces.  Value product: lane = channel pair, token rows read in
+// batches of VB = 32, so a chunk's values take two memory round trips (with batches of 8 the
+// chunk's round trips made the BF16 work-groups the last to finish on the 8 x 32768-token
+// layer).  Slots that hold no token are masked by a wave-uniform ballot; their (possibly
+// uninitialised) rows never reach the sums.
 template <int G>
 __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int kvh, int sl, int split, int ch0, int ch1,
                            const float* qf, float (*pbuf)[64]) {
   constexpr int KB = (G == 8) ? 4 : 8;    // key pieces in flight per lane
-  constexpr int VB = 8;                  // value rows in flight
+  constexpr int VB = 32;                 // value rows in flight
+  static_assert(64 % VB == 0 && VB < 64, "the row mask below shifts 1 by VB bits of a 64-bit word");
   const int lane = threadIdx.x;
   const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
   const uint16_t* kring = a.ring + ring_head;
