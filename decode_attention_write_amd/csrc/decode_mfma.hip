@@ -71,48 +71,52 @@ __host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
 }
 
 // ------------------------------------------------------------------ query preparation
-// One (KV head, sequence of the chunk) per 256-thread work-group.
+// One (KV head, sequence of the chunk, head block of up to 4 query heads) per 256-thread
+// work-group: GQA 8 takes two work-groups per unit, each with the operands of its head block.
 template <int G>
-__device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl) {
+__host__ __device__ constexpr int qprep_heads() { return G < 4 ? G : 4; }
+template <int G>
+__device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl, int hb) {
+  constexpr int GB = qprep_heads<G>();
   const int tid = threadIdx.x;
   const DecodeSeq sq = a.seqs[sl];
-  __shared__ float qf[G][D];
-  __shared__ float sig[G];
-  __shared__ float qt[G][2];
+  __shared__ float qf[GB][D];
+  __shared__ float sig[GB], rsig[GB];
+  __shared__ float qt[GB][2];
   const float* rot = reinterpret_cast<const float*>(a.rot + static_cast<size_t>(kvh) * ROT_HEAD_BYTES);
-  const uint16_t* q = a.q + (static_cast<size_t>(sq.src) * a.hq + static_cast<size_t>(kvh) * G) * D;
+  const uint16_t* q = a.q + (static_cast<size_t>(sq.src) * a.hq + static_cast<size_t>(kvh) * G + 4 * hb) * D;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.part) + qprep_offset(a) + (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
   // q' = q R: thread (half, c) reads column c of rows [64 half, 64 half + 64) once (coalesced)
-  // for all G heads; its 64 loads are issued before the query is staged, so the two latencies
-  // overlap; the two halves are added through LDS
+  // for the block's heads; its 64 loads are issued before the query is staged, so the two
+  // latencies overlap; the two halves are added through LDS
   const int c = tid & (D - 1), half = tid >> 7;
   float rcol[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) rcol[i] = rot[(64 * half + i) * D + c];
-  __shared__ float qin[G][D];
-  for (int idx = tid; idx < G * D; idx += 256) qin[idx / D][idx % D] = bf16_to_f32(q[idx]);
+  __shared__ float qin[GB][D];
+  for (int idx = tid; idx < GB * D; idx += 256) qin[idx / D][idx % D] = bf16_to_f32(q[idx]);
   __syncthreads();
   {
-    __shared__ float part[2][G][D];
-    float acc[G];
+    __shared__ float part[2][GB][D];
+    float acc[GB];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+    for (int h = 0; h < GB; ++h) acc[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 64; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(qin[h][64 * half + i], rcol[i], acc[h]);
+      for (int h = 0; h < GB; ++h) acc[h] = fmaf(qin[h][64 * half + i], rcol[i], acc[h]);
 #pragma unroll
-    for (int h = 0; h < G; ++h) part[half][h][c] = acc[h];
+    for (int h = 0; h < GB; ++h) part[half][h][c] = acc[h];
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < GB * D; idx += 256) {
       const int h = idx / D, cc = idx % D;
       qf[h][cc] = (part[0][h][cc] + part[1][h][cc]) * a.scale_log2;
     }
   }
   __syncthreads();
-  for (int h = tid >> 6; h < G; h += 4) {
+  if ((tid >> 6) < GB) {
     // one wave per head: sigma = max|q'| / 127, per-group sums
-    const int l = tid & 63;
+    const int h = tid >> 6, l = tid & 63;
     float mx = fmaxf(fabsf(qf[h][l]), fabsf(qf[h][l + 64]));
     float s0 = qf[h][l], s1 = qf[h][l + 64];
 #pragma unroll
@@ -123,15 +127,16 @@ __device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl) {
     }
     if (l == 0) {
       sig[h] = (mx > 0.0f) ? mx / 127.0f : 1.0f;
+      rsig[h] = (mx > 0.0f) ? 127.0f / mx : 1.0f;
       qt[h][0] = s0;
       qt[h][1] = s1;
     }
   }
   __syncthreads();
-  float* wf = reinterpret_cast<float*>(ws + QP_QF);
-  for (int idx = tid; idx < G * D; idx += 256) wf[idx] = qf[idx / D][idx % D];
-  float* wc = reinterpret_cast<float*>(ws + QP_CONST);
-  if (tid < G) {
+  float* wf = reinterpret_cast<float*>(ws + QP_QF) + 4 * hb * D;
+  for (int idx = tid; idx < GB * D; idx += 256) wf[idx] = qf[idx / D][idx % D];
+  float* wc = reinterpret_cast<float*>(ws + QP_CONST) + 3 * 4 * hb;
+  if (tid < GB) {
     wc[3 * tid + 0] = sig[tid] / 128.0f;
     wc[3 * tid + 1] = qt[tid][0] * 128.0f / sig[tid];
     wc[3 * tid + 2] = qt[tid][1] * 128.0f / sig[tid];
@@ -139,38 +144,45 @@ __device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl) {
   // group counter of the unit: the first two groups of every split are taken
   int32_t* ctr = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(a.part) + counter_offset(a)) +
                  (static_cast<size_t>(sl) * a.hkv + kvh) * a.n_split_max;
-  if (tid == 0) ctr[0] = 2 * int2_splits(sq.n_int2, a.pages_per_split);
-  // A operands: head block hb, lane l: row m = l % 16 = 4 (2 tau + grp) + h4, K-step g covers
-  // channels 64 g + 16 (l / 16) + j, j = 0..15 (byte j of the lane's 16 bytes)
-  constexpr int HB = (G + 3) / 4;
-  int8_t* wa = reinterpret_cast<int8_t*>(ws + QP_AOPS);
-  for (int idx = tid; idx < HB * 64 * 2 * 16; idx += 256) {
-    const int j = idx & 15, g = (idx >> 4) & 1, l = (idx >> 5) & 63, hb = idx >> 11;
-    const int m = l & 15, tau = m >> 3, grp = (m >> 2) & 1, h = 4 * hb + (m & 3);
-    int8_t v = 0;
-    if (grp == g && h < G) {
-      const int c = 64 * g + 16 * (l >> 4) + j;
-      const float x = qf[h][c] / sig[h];
-      const float t1 = rintf(x);
-      v = static_cast<int8_t>(tau == 0 ? t1 : rintf((x - t1) * 128.0f));
+  if (hb == 0 && tid == 0) ctr[0] = 2 * int2_splits(sq.n_int2, a.pages_per_split);
+  // A operands of head block hb: lane l: row m = l % 16 = 4 (2 tau + grp) + h4, K-step g covers
+  // channels 64 g + 16 (l / 16) + j, j = 0..15 (byte j of the lane's 16 bytes).  Thread t builds
+  // 32-bit words t and t + 256 of the block's 2048 bytes: word w holds bytes j = 4 (w % 4) ..
+  // 4 (w % 4) + 3 of (g, l) = ((w / 4) % 2, w / 8), four channels of one head
+  uint32_t* wa = reinterpret_cast<uint32_t*>(ws + QP_AOPS) + 512 * hb;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int w = tid + 256 * r;
+    const int g = (w >> 2) & 1, l = w >> 3;
+    const int m = l & 15, tau = m >> 3, grp = (m >> 2) & 1, h = m & 3;
+    uint32_t word = 0u;
+    if (grp == g && h < GB) {
+      const int c0 = 64 * g + 16 * (l >> 4) + 4 * (w & 3);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float x = qf[h][c0 + b] * rsig[h];
+        const float t1 = rintf(x);
+        const int v = static_cast<int>(tau == 0 ? t1 : rintf((x - t1) * 128.0f));
+        word |= (static_cast<uint32_t>(v) & 0xFFu) << (8 * b);
+      }
     }
-    wa[idx] = v;
+    wa[w] = word;
   }
 }
 
-// Grid (KV heads, sequences of the chunk), 256 threads.
+// Grid (KV heads, sequences of the chunk, head blocks), 256 threads.
 template <int G>
-__global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) { qprep_block<G>(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(256) void k_qprep(DecodeArgs a) { qprep_block<G>(a, blockIdx.x, blockIdx.y, blockIdx.z); }
 
 // The decode step's write and the query preparation in one launch: grid (KV heads, sequences,
-// 2), z = 0 the write of one (KV head, sequence), z = 1 its query preparation.  The two touch
-// disjoint memory (ring and pool; query, workspace), so they run side by side.  The write lands
-// in the ring before the split kernel, which runs after this launch on the same stream, reads it
-// (the new token attends to itself).
+// 1 + head blocks), z = 0 the write of one (KV head, sequence), z >= 1 the query preparation of
+// head block z - 1.  The two touch disjoint memory (ring and pool; query, workspace), so they
+// run side by side.  The write lands in the ring before the split kernel, which runs after this
+// launch on the same stream, reads it (the new token attends to itself).
 template <int G>
 __global__ __launch_bounds__(256) void k_step_qprep(StepArgs w, DecodeArgs a) {
   if (blockIdx.z == 0) step_write_block(w, blockIdx.x, blockIdx.y);
-  else qprep_block<G>(a, blockIdx.x, blockIdx.y);
+  else qprep_block<G>(a, blockIdx.x, blockIdx.y, blockIdx.z - 1);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -326,7 +338,6 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   const int kvh = unit % a.hkv, sl = unit / a.hkv;
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
   const DecodeSeq sq = a.seqs[sl];
-  const int n_pages = (sq.n_int2 + PAGE - 1) / PAGE;
   const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
   const int n_bsplits = bf16_splits(sq.n_int2, sq.len, a.pages_per_split, 0);
   // the BF16 sink + window tokens (partial records n_isplits ..) are done first by INT2 split 0
@@ -737,8 +748,9 @@ int decode_resident_workgroups(int gqa, int kernel) {
 
 template <int G>
 static hipError_t launch_g(const StepArgs* w, const DecodeArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  if (w) hipLaunchKernelGGL(k_step_qprep<G>, dim3(a.hkv, a.n_seqs, 2), dim3(256), 0, s, *w, a);
-  else hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs), dim3(256), 0, s, a);
+  constexpr int HB = (G + 3) / 4;   // query-preparation work-groups per unit
+  if (w) hipLaunchKernelGGL(k_step_qprep<G>, dim3(a.hkv, a.n_seqs, 1 + HB), dim3(256), 0, s, *w, a);
+  else hipLaunchKernelGGL(k_qprep<G>, dim3(a.hkv, a.n_seqs, HB), dim3(256), 0, s, a);
   if (t0) {
     const hipError_t e = hipEventRecord(t0, s);
     if (e != hipSuccess) return e;
