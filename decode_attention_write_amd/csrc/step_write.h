@@ -11,6 +11,17 @@
 
 namespace oscar {
 
+// ------------------------------------------------------------------ single-token key rotation
+// Output channel c of one key's rotation, shift_c + sum_i k_i R_ic, with column c of R in
+// registers: four interleaved partial sums (i mod 4) added at the end, so the 128 fused
+// multiply-adds form four independent chains instead of one.
+__device__ inline float rotate_channel(const float* kin, const float* rc, float shift) {
+  float p[4] = {shift, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < D; ++i) p[i & 3] = fmaf(kin[i], rc[i], p[i & 3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
 // ------------------------------------------------------------------ eviction
 // One token of one (sequence, KV head) moves from the window to INT2: INT2 index i takes ring
 // slot 64 + i % 256 (the oldest window token).  256 threads: thread t holds channel t % 128 of
@@ -106,9 +117,7 @@ __device__ inline void step_write_block(const StepArgs& a, int kvh, int sl) {
   if (sq.evict) evict_one(a.pool, a.hkv, sq.page, kvh, sq.n_int2, xv, codes, meta);
   __syncthreads();
   if (tid < D) {
-    float acc = shift;
-#pragma unroll
-    for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
+    const float acc = rotate_channel(kin, rc, shift);
     const size_t ring_head = (static_cast<size_t>(sq.seq) * a.hkv + kvh) * 2 * RING * D;
     const int p = sq.len0;
     const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;

@@ -491,9 +491,7 @@ __global__ __launch_bounds__(128) void k_append(WriteArgs a) {
     __syncthreads();
     kin[c] = bf16_to_f32(a.k[src + c]);
     __syncthreads();
-    float acc = shift;  // -(mu . R)_c: the key mean's shift (+0 without a mean)
-#pragma unroll
-    for (int i = 0; i < D; ++i) acc = fmaf(kin[i], rc[i], acc);
+    const float acc = rotate_channel(kin, rc, shift);  // shift: -(mu . R)_c, +0 without a key mean
     const int p = sq.len0 + t;
     const int slot = (p < SINK) ? p : SINK + (p - SINK) % WIN;
     a.ring[ring_head + static_cast<size_t>(slot) * D + c] = f32_to_bf16(acc);
