@@ -9,6 +9,8 @@
 // unrotated scores because R_K is orthogonal.  Split-K over pages with an exact
 // (m, l, o) merge is this library's work decomposition; the pages do not
 // describe one.
+#include <algorithm>
+
 #include "common.h"
 
 namespace oscar {
@@ -182,40 +184,47 @@ __global__ __launch_bounds__(256) void k_decode_simple(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
-// Grid (q heads, sequences of this chunk), 512 threads: out = sum_i 2^(m_i - M) o_i / sum_i
-// 2^(m_i - M) l_i over the unit's records i.  Thread (slice, c) takes channel c of the records
-// 16 slice + 64 k + j (j < 16) with a running maximum of its own, so that all 16 records' loads
-// of a pass are issued at once and nothing waits for a maximum over the whole unit; the four
-// slices are then merged.
+// Grid (q heads, sequences of this chunk), S x 128 threads (S = 1 .. 4 slices, enough for the
+// call's records in one pass where possible): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
+// over the unit's records i.  Thread (slice, c) takes channel c of the records 16 slice + 16 S k
+// + j (j < 16) with a running maximum of its own, so that all 16 records' loads of a pass are
+// issued at once and nothing waits for a maximum over the whole unit; the slices are then
+// merged.  The weights use the hardware exp2 (arguments <= 0; results below 2^-126 flush to 0).
 
 constexpr int COMBINE_SLICES = 4, COMBINE_BATCH = 16;
 
 __global__ __launch_bounds__(COMBINE_SLICES * D) void k_combine(DecodeArgs a) {
-  const int h = blockIdx.x, sl = blockIdx.y, c = threadIdx.x & (D - 1), slice = threadIdx.x >> 7;
+  // a slice is two whole waves: its index is wave-uniform
+  const int h = blockIdx.x, sl = blockIdx.y, c = threadIdx.x & (D - 1);
+  const int slice = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 7));
+  const int n_slices = blockDim.x >> 7;
   const DecodeSeq sq = a.seqs[sl];
   const int n = unit_records(sq.n_int2, sq.len, a.pages_per_split, a.kernel);
   const float* rec0 = a.part + (static_cast<size_t>(sl) * a.hq + h) * a.n_split_max * PART_STRIDE;
+  // (m, l) of a record are wave-uniform: read through the scalar cache (the records were written
+  // by an earlier launch), leaving the vector loads to the channel values
+  const __attribute__((address_space(4))) float* rec0_s = (const __attribute__((address_space(4))) float*)(rec0);
   float M = -INFINITY, L = 0.0f, O = 0.0f;
-  for (int b = COMBINE_BATCH * slice; b < n; b += COMBINE_SLICES * COMBINE_BATCH) {
+  for (int b = COMBINE_BATCH * slice; b < n; b += n_slices * COMBINE_BATCH) {
     float m[COMBINE_BATCH], l[COMBINE_BATCH], o[COMBINE_BATCH];
 #pragma unroll
     for (int j = 0; j < COMBINE_BATCH; ++j) {
-      const float* rec = rec0 + static_cast<size_t>(min(b + j, n - 1)) * PART_STRIDE;  // in range
-      m[j] = rec[0];
-      l[j] = rec[1];
-      o[j] = rec[2 + c];
+      const size_t r = static_cast<size_t>(min(b + j, n - 1)) * PART_STRIDE;  // in range
+      m[j] = rec0_s[r];
+      l[j] = rec0_s[r + 1];
+      o[j] = rec0[r + 2 + c];
     }
     float mb = M;
 #pragma unroll
     for (int j = 0; j < COMBINE_BATCH; ++j)
       if (b + j < n) mb = fmaxf(mb, m[j]);
     if (mb == -INFINITY) continue;  // only empty records so far (m = -inf, l = 0, o = 0)
-    const float alpha = (M == -INFINITY) ? 0.0f : exp2f(M - mb);
+    const float alpha = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - mb);
     L *= alpha;
     O *= alpha;
 #pragma unroll
     for (int j = 0; j < COMBINE_BATCH; ++j) {
-      const float w = (b + j < n && m[j] != -INFINITY) ? exp2f(m[j] - mb) : 0.0f;
+      const float w = (b + j < n && m[j] != -INFINITY) ? __builtin_amdgcn_exp2f(m[j] - mb) : 0.0f;
       L = fmaf(w, l[j], L);
       O = fmaf(w, o[j], O);
     }
@@ -230,12 +239,10 @@ __global__ __launch_bounds__(COMBINE_SLICES * D) void k_combine(DecodeArgs a) {
   __syncthreads();
   if (slice != 0) return;
   float Mt = sm[0];
-#pragma unroll
-  for (int p = 1; p < COMBINE_SLICES; ++p) Mt = fmaxf(Mt, sm[p]);
+  for (int p = 1; p < n_slices; ++p) Mt = fmaxf(Mt, sm[p]);
   float Lt = 0.0f, Ot = 0.0f;
-#pragma unroll
-  for (int p = 0; p < COMBINE_SLICES; ++p) {
-    const float w = (sm[p] == -INFINITY) ? 0.0f : exp2f(sm[p] - Mt);
+  for (int p = 0; p < n_slices; ++p) {
+    const float w = (sm[p] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm[p] - Mt);
     Lt = fmaf(w, sls[p], Lt);
     Ot = fmaf(w, so[p][c], Ot);
   }
@@ -245,7 +252,8 @@ __global__ __launch_bounds__(COMBINE_SLICES * D) void k_combine(DecodeArgs a) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(COMBINE_SLICES * D), 0, s, a);
+  const int slices = std::min(COMBINE_SLICES, std::max(1, (a.n_split_max + COMBINE_BATCH - 1) / COMBINE_BATCH));
+  hipLaunchKernelGGL(k_combine, dim3(a.hq, a.n_seqs), dim3(slices * D), 0, s, a);
   return hipGetLastError();
 }
 
