@@ -400,7 +400,10 @@ int oscar_kv_set_decode_kernel(oscar_kv *kv, int32_t kernel);
  *                       preparation or the combine);
  *   OSCAR_TIMED_WRITE   the write kernel of oscar_kv_write (not the page-table
  *                       upload).
- * enable = 0 destroys the events.  Returns OSCAR_E_ARG on a null handle,
+ * The recorded events sit between that kernel and its neighbours on the stream:
+ * each adds a few microseconds of gap on the GPU (kernels otherwise start back to
+ * back) and the measured interval includes the kernel's dispatch latency, so time
+ * whole calls with timing off.  enable = 0 destroys the events.  Returns OSCAR_E_ARG on a null handle,
  * OSCAR_E_STATE for a plan-only store, OSCAR_E_HIP if event creation fails (then
  * timing stays off). */
 #define OSCAR_TIMING_PAIRS 4096
