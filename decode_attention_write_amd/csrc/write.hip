@@ -280,10 +280,12 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
   // registers to LDS and the loads of the one after it are issued: in flight for a whole tile of
   // rotation and quantization.  Loads are never
   // conditional (rows past the call's tokens re-read the last row and are zeroed when stored; past
-  // the work-group's last tile the last tile is read again), which keeps the compiler's waits on
-  // them counted ones.  The tile's base is uniform; each lane adds a 32-bit byte offset.
-  auto issue = [&](int t, v4u_w* kw, v4u_w* vw) {
-    const int nh = min(PAGE, a.n_new - t * PAGE);
+  // the work-group's last tile every lane reads the first row of its last tile, whose registers
+  // are then never used: 512 bytes instead of a tile), which keeps the compiler's waits on them
+  // counted ones.  The tile's base is uniform; each lane adds a 32-bit byte offset.
+  auto issue = [&](int t_req, v4u_w* kw, v4u_w* vw) {
+    const int t = min(t_req, tile1 - 1);
+    const int nh = (t_req >= tile1) ? 1 : min(PAGE, a.n_new - t * PAGE);
     const size_t base = ((static_cast<size_t>(sq.src) * a.n_new + static_cast<size_t>(t) * PAGE) * a.hkv + kvh) * D * 2;
     const char* kb = reinterpret_cast<const char*>(a.k) + base;
     const char* vb = reinterpret_cast<const char*>(a.v) + base;
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
   v4u_w kreg[2], vreg[2];
   issue(tile0, kreg, vreg);
   stash(tile0, kreg, vreg);
-  issue(min(tile0 + 1, tile1 - 1), kreg, vreg);
+  issue(tile0 + 1, kreg, vreg);
   for (int tile = tile0; tile < tile1; ++tile) {
     const int n_here = min(PAGE, a.n_new - tile * PAGE);
     const int p0 = sq.len0 + tile * PAGE;
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(512, 4) void k_write(WriteArgs a) {
 
     // the next tile into LDS (loaded during the previous tile), then the loads of the one after
     stash(min(tile + 1, tile1 - 1), kreg, vreg);
-    issue(min(tile + 2, tile1 - 1), kreg, vreg);
+    issue(tile + 2, kreg, vreg);
 
     if (n_q > 0) {
       uint32_t* blk = reinterpret_cast<uint32_t*>(a.pool + (static_cast<size_t>(page) * a.hkv + kvh) * HEAD_BLOCK);
