@@ -542,7 +542,13 @@ def main():
     qs = [torch.from_numpy(synth.decode_queries(cfg, l, B, hq, hkv).view(np.int16)).cuda() for l in range(n_layers)]
     seqs = list(range(B))
     outs = [torch.empty((B, hq, 128), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
-    ws_bytes = max(st.workspace_bytes(seqs) for st in stores) + (1 << 20)
+    # sized for both decode modes (the deterministic one plans its own split size)
+    ws_bytes = max(st.workspace_bytes(seqs) for st in stores)
+    for st in stores:
+        st.set_decode_deterministic(True)
+    ws_bytes = max(ws_bytes, max(st.workspace_bytes(seqs) for st in stores)) + (1 << 20)
+    for st in stores:
+        st.set_decode_deterministic(False)
     ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(128)
 

@@ -240,6 +240,12 @@ int64_t choose_pages_per_split(const oscar_kv* kv, int32_t n_seqs, const std::ve
       if (wgs_for(pps) <= budget) break;
     best = std::max(best, pps);
   }
+  // Fixed page ranges (the deterministic mode) cannot move work between the splits of a unit:
+  // with two residency rounds of half the size, the dispatcher gives the second round to the
+  // slots that finish first.  Measured on the 100000 x 32 layer (142 pages per split in one
+  // round): split kernel 404-410 us against 376-380 us at 71; no gain where a split holds
+  // fewer pages (8 x 32768 at 13 -> 7 or 9, ragged GQA-8 at 87 -> 44).
+  if (kv->deterministic && kv->decode_kernel == 0 && best >= 100) best = ceil_div(best, 2);
   return best;
 }
 

@@ -226,7 +226,7 @@ def test_workspace_bytes_and_split_choice():
     s.set_decode_split(4)
     # the reference kernel keeps one BF16 record per unit: 5 + 1
     assert s.workspace_bytes([0, 1]) == expect(6)
-    s.set_decode_deterministic(True)   # the page-sharing switch does not change the plan
+    s.set_decode_deterministic(True)   # with an explicit split size the mode does not change the plan
     assert s.workspace_bytes([0, 1]) == expect(6)
     for bad in (-1, 2):
         with pytest.raises(oscar.OscarError) as e:
