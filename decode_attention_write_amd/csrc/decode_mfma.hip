@@ -484,10 +484,11 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float y = fmaf(lk1, cst[h][2], fmaf(lk0, cst[h][1], fmaf(sk1, x1[h], sk0 * x0[h])));
-      const float sc = valid ? y * cst[h][0] : -INFINITY;
-      z[h] = sc - m_run[h];
+      // score minus the running maximum in one fused step (+inf while the maximum is -inf,
+      // which sends the page through the rescale below)
+      z[h] = valid ? fmaf(y, cst[h][0], -m_run[h]) : -INFINITY;
       zmax = fmaxf(zmax, z[h]);
-      x0[h] = sc;  // keep the score for the rescale path
+      x0[h] = y;  // the unscaled dot, for the rescale path
     }
     if (__any(zmax > static_cast<float>(LAZY))) {
       // the running maximum is stale by more than 2^LAZY: move it to the exact maximum so far
@@ -495,11 +496,12 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
       float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        const float sc = valid ? x0[h] * cst[h][0] : -INFINITY;
         const float mn = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-            __builtin_bit_cast(int, fmaxf(m_run[h], lane_max(x0[h])))));
+            __builtin_bit_cast(int, fmaxf(m_run[h], lane_max(sc)))));
         alpha[h] = (m_run[h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run[h] - mn);
         m_run[h] = mn;
-        z[h] = x0[h] - mn;
+        z[h] = sc - mn;
         l_acc[h] *= alpha[h];
         lo_acc[0][h] *= alpha[h];
         lo_acc[1][h] *= alpha[h];
