@@ -46,9 +46,6 @@ constexpr int QP_QF = 4096;       // fp32 q' (scaled to log2 units) [head][128]
 constexpr int QP_CONST = 8192;    // fp32 per head: c_h = sigma_h / 128, Qt0'' , Qt1''
 constexpr int QP_STRIDE = QPREP_STRIDE;
 
-__host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
-  return static_cast<size_t>(a.n_seqs) * a.hq * a.n_split_max * PART_STRIDE * sizeof(float);
-}
 // Work sharing between the INT2 splits of one (sequence, KV head): the unit's full pages are
 // cut into groups of share_group<G>() pages, one group per step of the page loop.  Work-group
 // s starts on groups s and n_splits + s; every further group is handed out through one
@@ -64,11 +61,6 @@ __host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
 // before its page loop.
 template <int G>
 __host__ __device__ constexpr int share_group() { return 3; }
-
-// Per (sequence of the chunk, KV head): one page counter per split.
-__host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
-  return qprep_offset(a) + static_cast<size_t>(a.n_seqs) * a.hkv * QP_STRIDE;
-}
 
 // ------------------------------------------------------------------ query preparation
 // One (KV head, sequence of the chunk, head block of up to 4 query heads) per 256-thread
@@ -327,40 +319,19 @@ __device__ inline void bf16_split(const DecodeArgs& a, const DecodeSeq& sq, int 
 // XCDs' speeds).  The page sharing within a unit then evens out the rest.
 // Records 0 .. n_isplits-1 are INT2 page ranges, record n_isplits the BF16 sink + window.
 
+// The page work of INT2 split `split` of one unit, written to record `split`: split 0 first does
+// the folded BF16 work and the partially filled last page.
 template <int G>
-// Occupancy target: 3 waves per SIMD (2 for GQA 8, whose P.V needs twice the operands).
-__global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a) {
+__device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl, const DecodeSeq& sq, int split,
+                                           bool fold, int n_isplits, float (*pbuf_bf)[64]) {
   constexpr int GP = G < 4 ? 4 : G;       // heads padded to a multiple of 4
   constexpr int HB = GP / 4;              // head blocks (MFMA row blocks of Q.K)
-  const int n_units = a.hkv * a.n_seqs;
-  const int y = blockIdx.y;   // the unit's work-group index, in dispatch order
-  const int unit = (static_cast<int>(blockIdx.x) + n_units - y % n_units) % n_units;
-  const int kvh = unit % a.hkv, sl = unit / a.hkv;
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
-  const DecodeSeq sq = a.seqs[sl];
-  const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
-  const int n_bsplits = bf16_splits(sq.n_int2, sq.len, a.pages_per_split, 0);
-  // the BF16 sink + window tokens (partial records n_isplits ..) are done first by INT2 split 0
-  // (the unit's oldest work-group) when the plan folds them, else by work-groups of their own,
-  // dispatched before the INT2 splits: work-groups dispatched last issue last and would finish
-  // last with work that nobody can share
-  const bool fold = bf16_folded(sq.n_int2, sq.len, a.pages_per_split, 0);
-  const int nbw = fold ? 0 : n_bsplits;
-  if (y >= n_isplits + nbw) return;
-  const int split = y - nbw;  // INT2 split; negative for a BF16 work-group
-
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
                       (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
-  __shared__ float pbuf_bf[G][64];
   // P operand staging: hi rows (group, head) then lo rows; GQA <= 4: hi 0..7, lo 8..15,
   // GQA 8: hi 0..15, lo 16..31
   __shared__ _Float16 plds[32][64];
-  if (split < 0) {
-    const int b = y;
-    bf16_split<G>(a, sq, kvh, sl, n_isplits + b, (RING_CHUNKS * b) / n_bsplits, (RING_CHUNKS * (b + 1)) / n_bsplits,
-                  reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
-    return;
-  }
 
   // ---- prologue: query operands (kept in LDS and read per page, which leaves the registers
   // for a third page buffer) and per-head constants
@@ -714,6 +685,39 @@ __global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a
   }
 }
 
+
+template <int G>
+// Occupancy target: 3 waves per SIMD (2 for GQA 8, whose P.V needs twice the operands).
+__global__ __launch_bounds__(64, G == 8 ? 2 : 3) void k_decode_mfma(DecodeArgs a) {
+  const int n_units = a.hkv * a.n_seqs;
+  const int y = blockIdx.y;   // the unit's work-group index, in dispatch order
+  const int unit = (static_cast<int>(blockIdx.x) + n_units - y % n_units) % n_units;
+  const int kvh = unit % a.hkv, sl = unit / a.hkv;
+  const int lane = threadIdx.x;
+  const DecodeSeq sq = a.seqs[sl];
+  const int n_isplits = int2_splits(sq.n_int2, a.pages_per_split);
+  const int n_bsplits = bf16_splits(sq.n_int2, sq.len, a.pages_per_split, 0);
+  // the BF16 sink + window tokens (partial records n_isplits ..) are done first by INT2 split 0
+  // (the unit's oldest work-group) when the plan folds them, else by work-groups of their own,
+  // dispatched before the INT2 splits: work-groups dispatched last issue last and would finish
+  // last with work that nobody can share
+  const bool fold = bf16_folded(sq.n_int2, sq.len, a.pages_per_split, 0);
+  const int nbw = fold ? 0 : n_bsplits;
+  if (y >= n_isplits + nbw) return;
+  const int split = y - nbw;  // INT2 split; negative for a BF16 work-group
+
+  __shared__ float pbuf_bf[G][64];
+  if (split < 0) {
+    const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
+                        (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
+    const int b = y;
+    bf16_split<G>(a, sq, kvh, sl, n_isplits + b, (RING_CHUNKS * b) / n_bsplits, (RING_CHUNKS * (b + 1)) / n_bsplits,
+                  reinterpret_cast<const float*>(ws + QP_QF), pbuf_bf);
+    return;
+  }
+  int2_split<G>(a, kvh, sl, sq, split, fold, n_isplits, pbuf_bf);
+}
+
 // Work-groups to plan for one residency round: all wave slots of the device but one per
 // compute unit.  Measured on the 100000-token, 32-sequence, 8-KV-head decode: work-groups that
 // fill every slot (12 per CU) ran about 15% slower per page than 11 per CU.
@@ -757,7 +761,7 @@ static hipError_t launch_g(const StepArgs* w, const DecodeArgs& a, hipStream_t s
     const hipError_t e = hipEventRecord(t0, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_decode_mfma<G>, dim3(a.hkv * a.n_seqs, a.n_split_max), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_decode_mfma<G>, dim3(a.hkv * a.n_seqs, a.wg_rows), dim3(64), 0, s, a);
   if (t1) {
     const hipError_t e = hipEventRecord(t1, s);
     if (e != hipSuccess) return e;

@@ -101,6 +101,7 @@ struct DecodeArgs {
   int32_t kernel;         // 0 matrix-core split kernel, 1 reference kernel (record layout)
   int32_t share;          // matrix-core kernel: 1 = splits of a unit share their pages, 0 = fixed ranges
   int32_t out_bf16;       // 1: out holds bf16 (round to nearest even) instead of fp32
+  int32_t wg_rows;        // matrix-core kernel: grid rows (the work-groups of the largest unit)
   DecodeSeq seqs[CHUNK];
 };
 
@@ -163,5 +164,15 @@ hipError_t scratch_on_current_device(void** ptr);
 // bytes of the prepared-query area that follows the split partials in the workspace,
 // per (sequence of a launch chunk, KV head)
 constexpr int QPREP_STRIDE = 8448;
+
+// Workspace of one decode launch: the partial records [n_seqs][hq][n_split_max][130], the
+// prepared queries [n_seqs][hkv][QPREP_STRIDE bytes], then one int32 page counter per (unit,
+// record) slot.
+__host__ __device__ inline size_t qprep_offset(const DecodeArgs& a) {
+  return static_cast<size_t>(a.n_seqs) * a.hq * a.n_split_max * PART_STRIDE * sizeof(float);
+}
+__host__ __device__ inline size_t counter_offset(const DecodeArgs& a) {
+  return qprep_offset(a) + static_cast<size_t>(a.n_seqs) * a.hkv * QPREP_STRIDE;
+}
 
 }  // namespace oscar

@@ -748,6 +748,59 @@ def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
         assert np.array_equal(o, outs[("identity", key[1])]), key   # page order invariance
 
 
+@pytest.mark.parametrize("gqa", [1, 8])
+def test_ragged_launch_in_load_order(gpu_lib, gqa):
+    """A ragged launch (32 pages per split): one sequence of 120 full pages (4 splits of 30 pages)
+    beside seven of 3 pages and one without INT2 tokens.  The launch takes the sequences most
+    loaded first, so the heavy sequence, last in the call, is first in the launch and the output
+    rows come back through each sequence's own row.  The output matches the oracle on the same
+    cache state (rel-L2 <= 1e-3 per sequence), the deterministic mode to 1e-4 and a repeated call
+    to 1e-4.  A decode step (write in call order, attention in load order) then matches the
+    oracle on the state after it."""
+    hkv, hq = 2, 2 * gqa
+    lengths = [320 + 64 * 3 + 5] * 7 + [250, 320 + 64 * 120 + 17]
+    B, pps = len(lengths), 32
+    _case(f"ragged launch in load order, GQA {gqa}: 7 x {lengths[0]} + {lengths[7]} + {lengths[8]}")
+    cfg = synth.CFG_QWEN3_32B
+    rot = parity.calibrate(cfg, 5, hkv)
+    n_pages = sum(-(-max(0, L - 320) // 64) for L in lengths) + B
+    free = synth.page_permutation(cfg, 5, n_pages)
+    st = _store(gpu_lib, hq, hkv, B, 128, n_pages, free, rot)
+    kv = {}
+    for s, L in enumerate(lengths):
+        kv[s] = _kv_batch(cfg, [s], hkv, L + 1)
+        st.write([s], parity.to_dev_bf16(kv[s][0][:, :L]), parity.to_dev_bf16(kv[s][1][:, :L]))
+    st.set_decode_split(pps)
+    seqs = list(range(B))
+    qb = synth.decode_queries(cfg, 5, B, hq, hkv)
+    q = parity.to_dev_bf16(qb)
+    outs = [st.decode(seqs, q, SCALE).cpu().numpy() for _ in range(2)]
+    assert parity.rel_l2(outs[1], outs[0]) <= 1e-4
+    st.set_decode_deterministic(True)
+    ref_det = st.decode(seqs, q, SCALE).cpu().numpy()
+    st.set_decode_deterministic(False)
+    assert parity.rel_l2(outs[0], ref_det) <= 1e-4, parity.rel_l2(outs[0], ref_det)
+    gpu = parity.export(st)
+    lens = np.array([st.seq_info(s)[0] for s in seqs])
+    n2s = np.array([st.seq_info(s)[1] for s in seqs])
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], lens, n2s, rot, qb, seqs, SCALE, hq)
+    for b in range(B):
+        assert parity.rel_l2(outs[0][b], iso[b]) <= ISO_TOL, b
+    # decode step: one more token per sequence (evicting where the window is full)
+    kt = parity.to_dev_bf16(np.stack([kv[s][0][0, lengths[s]] for s in seqs]))
+    vt = parity.to_dev_bf16(np.stack([kv[s][1][0, lengths[s]] for s in seqs]))
+    qb2 = synth.decode_queries(cfg, 6, B, hq, hkv)
+    out2 = st.decode_step(seqs, kt, vt, parity.to_dev_bf16(qb2), SCALE).cpu().numpy()
+    gpu = parity.export(st)
+    lens = np.array([st.seq_info(s)[0] for s in seqs])
+    n2s = np.array([st.seq_info(s)[1] for s in seqs])
+    assert list(lens) == [L + 1 for L in lengths]
+    iso = attention.decode(gpu[0], gpu[1], gpu[2], lens, n2s, rot, qb2, seqs, SCALE, hq)
+    err = max(parity.rel_l2(out2[b], iso[b]) for b in range(B))
+    print(f"[parity] load order, GQA {gqa}: decode step rel-l2 vs oracle max {err:.2e}", flush=True)
+    assert err <= ISO_TOL
+
+
 def test_qwen3_4b_shape_small_context(gpu_lib):
     """32 q / 8 kv heads, batch 8, 2048-token context: prefill, then evict + append + attend."""
     hkv, hq, B, L = 8, 32, 8, 2048

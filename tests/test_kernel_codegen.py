@@ -46,9 +46,10 @@ def _kernel_meta(lines):
 
 
 def _page_loops(lines, symbol):
-    """Bodies of the kernel's outermost loops that stream INT2 pages: wide global loads feeding
+    """Bodies of the kernel's innermost loops that stream INT2 pages: wide global loads feeding
     matrix-core instructions (the BF16 sink/window loops use no matrix cores and wait per batch).
-    A loop is its header block plus every block the compiler annotates as inside it."""
+    A loop is its header block plus every block the compiler annotates as inside it (nested
+    loops carry their annotation on the comment lines after the label)."""
     start = next(i for i, ln in enumerate(lines) if ln.startswith(symbol + ":"))
     end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
     blocks, cur = [], None
@@ -59,17 +60,33 @@ def _page_loops(lines, symbol):
             blocks.append(cur)
         elif cur is not None:
             cur.append(ln)
-    loops = []
-    for b in blocks:
-        if "Loop Header: Depth=1" not in b[0]:
+    def head(b):
+        # the label line and the comment-only lines after it carry the loop annotations
+        out = [b[0]]
+        for ln in b[1:]:
+            if not re.match(r"^\s+;", ln):
+                break
+            out.append(ln)
+        return " ".join(out)
+
+    def label(b):
+        return b[0].split(":")[0][2:]  # .LBBx_y -> BBx_y
+
+    heads = [head(b) for b in blocks]
+    loops = {}
+    for b, h in zip(blocks, heads):
+        m = re.search(r"Loop Header: Depth=(\d+)", h)
+        if not m:
             continue
-        name = b[0].split(":")[0][2:]  # .LBBx_y -> BBx_y
-        body = [ln for x in blocks
-                if x is b or f"Header={name} Depth=1" in x[0] or f"Parent Loop {name} Depth=1" in x[0]
-                for ln in x]
+        name, depth = label(b), m.group(1)
+        members = [x for x, hx in zip(blocks, heads)
+                   if x is b or f"Header={name} Depth={depth}" in hx or f"Parent Loop {name} Depth={depth}" in hx]
+        body = [ln for x in members for ln in x]
         if any("global_load_dwordx4" in ln for ln in body) and any("v_mfma" in ln for ln in body):
-            loops.append(body)
-    return loops
+            loops[name] = (members, body)
+    # innermost: no other streaming loop's header among its blocks
+    return [body for name, (members, body) in loops.items()
+            if not any(label(x) in loops and label(x) != name for x in members)]
 
 
 def test_decode_split_kernel_codegen(tmp_path):
