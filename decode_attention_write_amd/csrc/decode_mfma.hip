@@ -329,8 +329,9 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
   const int lane = threadIdx.x, q4 = lane >> 4, n16 = lane & 15;
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.part) + qprep_offset(a) +
                       (static_cast<size_t>(sl) * a.hkv + kvh) * QP_STRIDE;
-  // P operand staging: hi rows (group, head) then lo rows; GQA <= 4: hi 0..7, lo 8..15,
-  // GQA 8: hi 0..15, lo 16..31
+  // P operand staging, one MFMA row block (16 rows) per block of rows: GQA <= 4: hi rows
+  // (group, head) 0..7, lo rows 8..15; GQA 8: per group g, rows 16 g + h (hi) and 16 g + 8 + h
+  // (lo), so that each group's block meets only that group's 64 value channels
   __shared__ _Float16 plds[32][64];
 
   // ---- prologue: query operands (kept in LDS and read per page, which leaves the registers
@@ -350,7 +351,8 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
     for (int k = 0; k < 3; ++k)
       cst[h][k] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wc[3 * h + k])));
   for (int i = lane; i < 32 * 64; i += 64) (&plds[0][0])[i] = static_cast<_Float16>(0.0f);
-  constexpr int LO_ROWS = (G == 8) ? 16 : 8;
+  // staging rows of head h: hi and lo residual of groups 0 and 1 (see plds)
+  constexpr int ROW_HI1 = (G == 8) ? 16 : GP, ROW_LO0 = 8, ROW_LO1 = (G == 8) ? 24 : 8 + GP;
 
   // token of this lane after the Q.K row merge (which pairs tiles 0/2 and 1/3): the lane index
   const int tok = lane;
@@ -477,7 +479,8 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
         lo_acc[0][h] *= alpha[h];
         lo_acc[1][h] *= alpha[h];
       }
-      // oacc row 4 q4 + r: G <= 4 -> head r (lanes 0-31); G = 8 -> head 4 (q4 % 2) + r
+      // oacc row 4 q4 + r: G <= 4 -> head r; G = 8 -> head 4 (q4 % 2) + r (hi rows in lanes
+      // 0-31, their lo residuals in lanes 32-63)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // values, not array elements, in the conditional: a conditional of two lvalues would
@@ -507,9 +510,9 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
       const float a0 = p * f0, a1 = p * f1;
       const _Float16 h0 = static_cast<_Float16>(a0), h1 = static_cast<_Float16>(a1);
       plds[h][tok] = h0;
-      plds[GP + h][tok] = h1;
-      plds[LO_ROWS + h][tok] = static_cast<_Float16>(a0 - static_cast<float>(h0));
-      plds[LO_ROWS + GP + h][tok] = static_cast<_Float16>(a1 - static_cast<float>(h1));
+      plds[ROW_HI1 + h][tok] = h1;
+      plds[ROW_LO0 + h][tok] = static_cast<_Float16>(a0 - static_cast<float>(h0));
+      plds[ROW_LO1 + h][tok] = static_cast<_Float16>(a1 - static_cast<float>(h1));
     }
     __syncthreads();
     // A operand rows (grp, h) = lane % 16: tokens 32 s + 8 (lane / 16) + 0..7
@@ -530,12 +533,11 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
       const uint32_t lo4 = w << 4, hi6 = w >> 6;
       const v8h b0 = as_h8(lo4 & 0x00300030u, lo4 & 0x00C000C0u, w & 0x00300030u, w & 0x00C000C0u);
       const v8h b1 = as_h8(w & 0x03000300u, hi6 & 0x00300030u, hi6 & 0x00C000C0u, hi6 & 0x03000300u);
-      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA0, b0, oacc[ct], 0, 0, 0);
-      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA1, b1, oacc[ct], 0, 0, 0);
-      if (G == 8) {  // lo residual rows of the 16 (group, head) rows
-        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB0, b0, oacc[ct], 0, 0, 0);
-        oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pB1, b1, oacc[ct], 0, 0, 0);
-      }
+      // GQA 8: group 0's row block for channel tiles 0..3, group 1's for 4..7
+      const v8h& xa0 = (G == 8 && ct >= 4) ? pB0 : pA0;
+      const v8h& xa1 = (G == 8 && ct >= 4) ? pB1 : pA1;
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa0, b0, oacc[ct], 0, 0, 0);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa1, b1, oacc[ct], 0, 0, 0);
     }
   };
 
@@ -654,19 +656,19 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
     losum[1][h] = lane_sum(lo_acc[1][h]);
   }
   const float two20 = __builtin_ldexpf(1.0f, 20 + LAZY);  // undoes pfac's 2^(e - 4 + LAZY)
-  if (G <= 4) {
-    // rows 8..15 (lanes 32..63) hold the lo-residual products of rows 0..7: fold them in
+  // rows 8..15 (lanes 32..63) of every row block hold the lo-residual products of rows 0..7:
+  // fold them in
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+  for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[ct][r] += __shfl_xor(oacc[ct][r], 32, 64);
-  }
+    for (int r = 0; r < 4; ++r) oacc[ct][r] += __shfl_xor(oacc[ct][r], 32, 64);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float* rec = a.part + ((static_cast<size_t>(sl) * a.hq + kvh * G + h) * a.n_split_max + split) * PART_STRIDE;
     if (lane == 0) { rec[0] = m_run[h]; rec[1] = lsum[h]; }
   }
-  // oacc[ct] row 4 q4 + r = grp * GP + h; channel 16 ct + n16 belongs to group ct / 4
+  // oacc[ct] row 4 q4 + r (< 8) = grp * 4 + h for GQA <= 4, h for GQA 8 (whose row block of
+  // channel tile ct is group ct / 4's); channel 16 ct + n16 belongs to group ct / 4
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
     const int grp = ct >> 2;
@@ -676,7 +678,7 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
       int h;
       bool mine;
       if (GP == 4) { h = row - 4 * grp; mine = (row >> 2) == grp && h < G; }
-      else { h = row - 8 * grp; mine = (row >> 3) == grp; }
+      else { h = row; mine = row < 8; }
       if (mine) {
         float* rec = a.part + ((static_cast<size_t>(sl) * a.hq + kvh * G + (h % G)) * a.n_split_max + split) * PART_STRIDE;
         rec[2 + 16 * ct + n16] = fmaf(oacc[ct][r], two20, losum[grp][h % G]);
