@@ -137,16 +137,22 @@ __device__ inline void qprep_block(const DecodeArgs& a, int kvh, int sl, int hb)
   int32_t* ctr = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(a.part) + counter_offset(a)) +
                  (static_cast<size_t>(sl) * a.hkv + kvh) * a.n_split_max;
   if (hb == 0 && tid == 0) ctr[0] = 2 * int2_splits(sq.n_int2, a.pages_per_split);
-  // A operands of head block hb: lane l: row m = l % 16 = 4 (2 tau + grp) + h4, K-step g covers
-  // channels 64 g + 16 (l / 16) + j, j = 0..15 (byte j of the lane's 16 bytes).  Thread t builds
-  // 32-bit words t and t + 256 of the block's 2048 bytes: word w holds bytes j = 4 (w % 4) ..
-  // 4 (w % 4) + 3 of (g, l) = ((w / 4) % 2, w / 8), four channels of one head
-  uint32_t* wa = reinterpret_cast<uint32_t*>(ws + QP_AOPS) + 512 * hb;
+  // A operands, 2048 bytes: lane l, K-step g (channels 64 g + 16 (l / 16) + j, j = 0..15 = byte
+  // j of the lane's 16 bytes); word w holds bytes j = 4 (w % 4) .. 4 (w % 4) + 3 of
+  // (g, l) = ((w / 4) % 2, w / 8), four channels of one row m = l % 16.
+  //   GQA <= 4: m = 4 (2 tau + grp) + h (rows of the other group's channels are zero); thread t
+  //   builds words t and t + 256.
+  //   GQA 8: m = 8 tau + h over the unit's 8 heads, both K-steps of every row non-zero (the
+  //   split kernel keeps one accumulator per group); head block hb builds the 256 words of its
+  //   heads' rows (bit 2 of l, bit 5 of w, equal to hb).
+  uint32_t* wa = reinterpret_cast<uint32_t*>(ws + QP_AOPS);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int w = tid + 256 * r;
+  for (int r = 0; r < (G == 8 ? 1 : 2); ++r) {
+    const int w = (G == 8) ? (((tid >> 5) << 6) | (hb << 5) | (tid & 31)) : tid + 256 * r;
     const int g = (w >> 2) & 1, l = w >> 3;
-    const int m = l & 15, tau = m >> 3, grp = (m >> 2) & 1, h = m & 3;
+    const int m = l & 15, tau = m >> 3;
+    const int grp = (G == 8) ? g : (m >> 2) & 1;
+    const int h = m & 3;   // head within the block (GQA 8: block (m >> 2) & 1 = hb)
     uint32_t word = 0u;
     if (grp == g && h < GB) {
       const int c0 = 64 * g + 16 * (l >> 4) + 4 * (w & 3);
@@ -336,12 +342,10 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
 
   // ---- prologue: query operands (kept in LDS and read per page, which leaves the registers
   // for a third page buffer) and per-head constants
-  __shared__ v4i aop_lds[HB][2][64];
+  __shared__ v4i aop_lds[2][64];   // [K-step][lane] (see qprep_block)
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-      aop_lds[hb][g][lane] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + ((hb * 64 + lane) * 2 + g) * 16);
+  for (int g = 0; g < 2; ++g)
+    aop_lds[g][lane] = *reinterpret_cast<const v4i*>(ws + QP_AOPS + (lane * 2 + g) * 16);
   // per-head constants are wave-uniform: keep them in scalar registers
   float cst[G][3];
   const float* wc = reinterpret_cast<const float*>(ws + QP_CONST);
@@ -409,7 +413,10 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
     const v4u& md = raw.md;
     const int n_valid = min(PAGE, sq.n_int2 - lp * PAGE);
 
-    // ---- Q.K on the matrix cores: acc[hb][t] rows (tau, grp, h4), columns = tokens of tile t
+    // ---- Q.K on the matrix cores, columns = tokens of tile t.  GQA <= 4: acc[0][t] rows
+    // (tau, grp, h), the two K-steps (channel groups) summed, the other group's rows of each
+    // K-step zero.  GQA 8: acc[g][t] rows (tau, h) of K-step g alone (one accumulator per group:
+    // half the instructions of a row layout with a zero half).
     v4i acc[HB][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -419,31 +426,39 @@ __device__ __forceinline__ void int2_split(const DecodeArgs& a, int kvh, int sl,
         const uint32_t w = kc[2 * (t & 1) + g];
         const v4i b = {static_cast<int>(w & 0x03030303u), static_cast<int>((w >> 2) & 0x03030303u),
                        static_cast<int>((w >> 4) & 0x03030303u), static_cast<int>((w >> 6) & 0x03030303u)};
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          if (g == 0) acc[hb][t] = v4i{0, 0, 0, 0};
-          acc[hb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop_lds[hb][g][lane], b, acc[hb][t], 0, 0, 0);
+        if (G == 8) {
+          acc[g][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop_lds[g][lane], b, v4i{0, 0, 0, 0}, 0, 0, 0);
+        } else {
+          if (g == 0) acc[0][t] = v4i{0, 0, 0, 0};
+          acc[0][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop_lds[g][lane], b, acc[0][t], 0, 0, 0);
         }
       }
     }
     // ---- merge rows across lanes: afterwards lane = token, x0/x1 = group 0/1 dot per head.
-    // Lane group q4 holds rows (tau, grp) = (q4 / 2, q4 % 2).  The 32-lane swaps of tiles 0/2
-    // and 1/3 put the tau = 0 rows of both tiles of a pair in one register and the tau = 1 rows
-    // in the other (lanes 0-31 the first tile, 32-63 the second); the two terms are merged in
-    // integers; the 16-lane swap then separates the groups, leaving tiles 0, 1, 2, 3 in lanes
-    // 0-15, 16-31, 32-47, 48-63.
+    // Lane group q4 holds rows (tau, s) = (q4 / 2, q4 % 2), where s is the group (GQA <= 4) or
+    // the head half (GQA 8).  The 32-lane swaps of tiles 0/2 and 1/3 put the tau = 0 rows of both
+    // tiles of a pair in one register and the tau = 1 rows in the other (lanes 0-31 the first
+    // tile, 32-63 the second); the two terms are merged in integers; the 16-lane swap then
+    // separates s, leaving tiles 0, 1, 2, 3 in lanes 0-15, 16-31, 32-47, 48-63.
     float x0[GP], x1[GP];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int a2 = 0; a2 < HB; ++a2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const auto s02 = __builtin_amdgcn_permlane32_swap(acc[hb][0][r], acc[hb][2][r], false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(acc[hb][1][r], acc[hb][3][r], false, false);
+        const auto s02 = __builtin_amdgcn_permlane32_swap(acc[a2][0][r], acc[a2][2][r], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(acc[a2][1][r], acc[a2][3][r], false, false);
         const int c02 = static_cast<int>((static_cast<uint32_t>(s02[0]) << 7) + static_cast<uint32_t>(s02[1]));
         const int c13 = static_cast<int>((static_cast<uint32_t>(s13[0]) << 7) + static_cast<uint32_t>(s13[1]));
         const auto gg = __builtin_amdgcn_permlane16_swap(c02, c13, false, false);
-        x0[4 * hb + r] = static_cast<float>(static_cast<int>(gg[0]));
-        x1[4 * hb + r] = static_cast<float>(static_cast<int>(gg[1]));
+        const float s_even = static_cast<float>(static_cast<int>(gg[0]));
+        const float s_odd = static_cast<float>(static_cast<int>(gg[1]));
+        if (G == 8) {   // accumulator a2 = group, s = head half
+          (a2 == 0 ? x0 : x1)[r] = s_even;
+          (a2 == 0 ? x0 : x1)[4 + r] = s_odd;
+        } else {        // s = group, head r
+          x0[r] = s_even;
+          x1[r] = s_odd;
+        }
       }
 
     // ---- scores (log2 units) and the running max
