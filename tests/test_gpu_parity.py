@@ -185,7 +185,7 @@ def test_tiny_config_write_and_decode(gpu_lib):
     _e2e(out, ref)
 
 
-@pytest.mark.parametrize("gqa", [1, 4, 8])
+@pytest.mark.parametrize("gqa", [1, 2, 4, 8])
 def test_edge_lengths_ragged_shuffled_pages(gpu_lib, gqa):
     """Lengths around every routing boundary, one prefill each, shuffled free list, one decode call."""
     hkv = 2
@@ -748,7 +748,7 @@ def test_split_count_invariance_determinism_page_order(gpu_lib, kernel):
         assert np.array_equal(o, outs[("identity", key[1])]), key   # page order invariance
 
 
-@pytest.mark.parametrize("gqa", [1, 8])
+@pytest.mark.parametrize("gqa", [1, 2, 4, 8])
 def test_ragged_launch_in_load_order(gpu_lib, gqa):
     """A ragged launch (32 pages per split): one sequence of 120 full pages (4 splits of 30 pages)
     beside seven of 3 pages and one without INT2 tokens.  The launch takes the sequences most
